@@ -1,0 +1,369 @@
+/*
+ * CPU oracle for the DeepSeek Sparse Attention (DSA) decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table
+ * or constant with the GPU path and is never called by it.
+ *
+ * Plain loops in float64, written from the definitions on these pages:
+ *  - "MTP and sparse attention: NSA and DSA", DSA bullet: the index score
+ *    I(t,s) = sum_j w(t,j) * ReLU(q(t,j) . k(s)) over 64 indexer heads of 128
+ *    dims, in FP8 with a 4-byte scale per cached key (the cache accounting
+ *    listing: 128 + 4 bytes per token); each query keeps its 2048
+ *    highest-scoring tokens and runs absorbed-form MLA over only those
+ *    (per-pair cost 2*H*(512+64) + 2*H*512: scores over the 576-wide latent,
+ *    values are its first 512 dims).
+ *  - "[SGLang] NSA", init_forward_metadata: cached lengths include the new
+ *    (draft) rows; in an extend of n rows onto a cache of L tokens, row i sees
+ *    L - n + 1 + i tokens (3 rows at L = 10 see 8, 9, 10).
+ *  - "[SGLang] NSA", NSAMetadata: page tables map a request's token
+ *    positions to physical pages of 64 tokens.
+ * Ties in the selection go to the lower position.  FP8 values are OCP
+ * e4m3fn (the pages say FP8 / E4M3 only; e4m3fn is the reading taken).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---- number formats ---------------------------------------------------- */
+
+/* OCP e4m3fn: sign, 4-bit exponent with bias 7, 3-bit mantissa.  Exponent
+ * field 0 holds subnormals m/8 * 2^-6; field 15 with mantissa 7 is NaN;
+ * there is no infinity. */
+double oracle_e4m3_decode(uint8_t c) {
+  int sign = (c >> 7) & 1;
+  int e = (c >> 3) & 15;
+  int m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_decode(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* ---- batch metadata ------------------------------------------------------ */
+
+typedef struct {
+  int32_t B;
+  const int32_t* cu_q;       /* [B+1] cumulative query rows */
+  const int32_t* seqlens_k;  /* [B]   cached tokens, new rows included */
+  const int32_t* page_table; /* [B * max_pages] */
+  int32_t max_pages;
+  int32_t page_size;
+} oracle_batch;
+
+int32_t oracle_row_request(const oracle_batch* bt, int32_t t) {
+  for (int32_t b = 0; b < bt->B; ++b)
+    if (t >= bt->cu_q[b] && t < bt->cu_q[b + 1]) return b;
+  return -1;
+}
+
+/* row j of request b sees L_b - n_b + 1 + j tokens */
+int64_t oracle_row_visible(const oracle_batch* bt, int32_t t) {
+  int32_t b = oracle_row_request(bt, t);
+  if (b < 0) return 0;
+  int64_t n = bt->cu_q[b + 1] - bt->cu_q[b];
+  int64_t j = t - bt->cu_q[b];
+  int64_t v = (int64_t)bt->seqlens_k[b] - n + 1 + j;
+  return v > 0 ? v : 0;
+}
+
+int64_t oracle_slot(const oracle_batch* bt, int32_t b, int64_t s) {
+  int64_t page = bt->page_table[(int64_t)b * bt->max_pages + s / bt->page_size];
+  return page * bt->page_size + s % bt->page_size;
+}
+
+/* ---- work splitting ------------------------------------------------------ */
+
+typedef void (*item_fn)(void* ctx, int64_t item);
+typedef struct {
+  item_fn fn;
+  void* ctx;
+  int64_t n;
+  int64_t next;
+  pthread_mutex_t mu;
+} pool_t;
+
+static void* pool_worker(void* p) {
+  pool_t* pl = (pool_t*)p;
+  for (;;) {
+    pthread_mutex_lock(&pl->mu);
+    int64_t i = pl->next++;
+    pthread_mutex_unlock(&pl->mu);
+    if (i >= pl->n) break;
+    pl->fn(pl->ctx, i);
+  }
+  return NULL;
+}
+
+/* Runs fn(ctx, i) for i in [0, n) on `threads` threads.  Items are
+ * independent and write disjoint outputs, so results do not depend on the
+ * thread count. */
+static void run_items(int64_t n, int threads, item_fn fn, void* ctx) {
+  if (threads <= 0) {
+    long c = sysconf(_SC_NPROCESSORS_ONLN);
+    threads = c > 0 ? (int)c : 1;
+  }
+  if (threads > 512) threads = 512;
+  if (threads > n) threads = (int)(n > 0 ? n : 1);
+  pool_t pl;
+  pl.fn = fn;
+  pl.ctx = ctx;
+  pl.n = n;
+  pl.next = 0;
+  pthread_mutex_init(&pl.mu, NULL);
+  if (threads == 1) {
+    pool_worker(&pl);
+  } else {
+    pthread_t th[512];
+    for (int i = 0; i < threads; ++i) pthread_create(&th[i], NULL, pool_worker, &pl);
+    for (int i = 0; i < threads; ++i) pthread_join(th[i], NULL);
+  }
+  pthread_mutex_destroy(&pl.mu);
+}
+
+/* ---- index score ----------------------------------------------------------
+ * I(t,s) = sum_h w(t,h) * max(0, sum_d q(t,h,d) * k(s,d)) with
+ * q = q_scale(t) * e4m3(q8), k = k_scale(s) * e4m3(k8); d and h summed in
+ * ascending order.  Written for s < v_t; other entries are left as they are.
+ */
+#define KEY_CHUNK 4096
+
+typedef struct {
+  const oracle_batch* bt;
+  int32_t H, D;
+  const uint8_t* q8;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k8;
+  const float* k_scale;
+  const int32_t* rows;
+  int32_t n_rows;
+  double* out;
+  int64_t ld;
+  int64_t chunks_per_row;
+} score_ctx;
+
+static void score_item(void* p, int64_t item) {
+  score_ctx* c = (score_ctx*)p;
+  int64_t i = item / c->chunks_per_row;
+  int64_t ch = item % c->chunks_per_row;
+  int32_t t = c->rows[i];
+  int32_t b = oracle_row_request(c->bt, t);
+  if (b < 0) return;
+  int64_t v = oracle_row_visible(c->bt, t);
+  int64_t s0 = ch * KEY_CHUNK, s1 = s0 + KEY_CHUNK < v ? s0 + KEY_CHUNK : v;
+  if (s0 >= s1) return;
+  int32_t H = c->H, D = c->D;
+  double* q = (double*)malloc(sizeof(double) * (size_t)H * (size_t)D);
+  double* k = (double*)malloc(sizeof(double) * (size_t)D);
+  double qs = (double)c->q_scale[t];
+  for (int64_t e = 0; e < (int64_t)H * D; ++e)
+    q[e] = qs * oracle_e4m3_decode(c->q8[(int64_t)t * H * D + e]);
+  for (int64_t s = s0; s < s1; ++s) {
+    int64_t slot = oracle_slot(c->bt, b, s);
+    double ks = (double)c->k_scale[slot];
+    for (int d = 0; d < D; ++d) k[d] = ks * oracle_e4m3_decode(c->k8[slot * D + d]);
+    double I = 0.0;
+    for (int h = 0; h < H; ++h) {
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d) dot += q[(int64_t)h * D + d] * k[d];
+      double relu = dot > 0.0 ? dot : 0.0;
+      I += (double)c->w[(int64_t)t * H + h] * relu;
+    }
+    c->out[i * c->ld + s] = I;
+  }
+  free(q);
+  free(k);
+}
+
+void oracle_index_score(const oracle_batch* bt, int32_t H, int32_t D, const uint8_t* q8,
+                        const float* q_scale, const float* w, const uint8_t* k8,
+                        const float* k_scale, const int32_t* rows, int32_t n_rows, double* out,
+                        int64_t ld, int threads) {
+  int64_t maxv = 0;
+  for (int32_t i = 0; i < n_rows; ++i) {
+    int64_t v = oracle_row_visible(bt, rows[i]);
+    if (v > maxv) maxv = v;
+  }
+  score_ctx c = {bt, H, D, q8, q_scale, w, k8, k_scale, rows, n_rows, out, ld,
+                 (maxv + KEY_CHUNK - 1) / KEY_CHUNK};
+  if (c.chunks_per_row == 0) return;
+  run_items((int64_t)n_rows * c.chunks_per_row, threads, score_item, &c);
+}
+
+/* ---- top-k -----------------------------------------------------------------
+ * Order the v visible positions by (score descending, position ascending)
+ * and keep the first K = min(k, v).  sel[0..K) holds them in that order and
+ * sel[K..k) = -1.  kth = score of the K-th kept position (NaN when K = 0).
+ * flags[s] (s < v) = 1 when |I(s) - kth| <= band * |kth|: positions whose
+ * membership a float32 score may legitimately flip.
+ */
+typedef struct {
+  double score;
+  int64_t pos;
+} scored_t;
+
+static int cmp_scored(const void* a, const void* b) {
+  const scored_t* x = (const scored_t*)a;
+  const scored_t* y = (const scored_t*)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return x->pos < y->pos ? -1 : (x->pos > y->pos ? 1 : 0);
+}
+
+int32_t oracle_topk(const double* scores, int64_t v, int32_t k, double band, int32_t* sel,
+                    uint8_t* flags, double* kth) {
+  int64_t K = v < k ? v : k;
+  if (K < 0) K = 0;
+  scored_t* a = (scored_t*)malloc(sizeof(scored_t) * (size_t)(v > 0 ? v : 1));
+  for (int64_t s = 0; s < v; ++s) {
+    a[s].score = scores[s] == 0.0 ? 0.0 : scores[s]; /* -0.0 counts as +0.0 */
+    a[s].pos = s;
+  }
+  qsort(a, (size_t)v, sizeof(scored_t), cmp_scored);
+  for (int64_t j = 0; j < k; ++j) sel[j] = j < K ? (int32_t)a[j].pos : -1;
+  double kv = K > 0 ? a[K - 1].score : NAN;
+  if (kth) *kth = kv;
+  if (flags) {
+    for (int64_t s = 0; s < v; ++s) {
+      double x = scores[s] == 0.0 ? 0.0 : scores[s];
+      flags[s] = (K > 0 && fabs(x - kv) <= band * fabs(kv)) ? 1 : 0;
+    }
+  }
+  free(a);
+  return (int32_t)K;
+}
+
+typedef struct {
+  const double* scores;
+  int64_t ld;
+  const int64_t* v;
+  int32_t k;
+  double band;
+  int32_t* sel;
+  uint8_t* flags;
+  int64_t ldf;
+  double* kth;
+  int32_t* K;
+} topk_ctx;
+
+static void topk_item(void* p, int64_t i) {
+  topk_ctx* c = (topk_ctx*)p;
+  int32_t K = oracle_topk(c->scores + i * c->ld, c->v[i], c->k, c->band, c->sel + i * c->k,
+                          c->flags ? c->flags + i * c->ldf : NULL, c->kth + i);
+  if (c->K) c->K[i] = K;
+}
+
+void oracle_topk_rows(const double* scores, int64_t ld, const int64_t* v, int32_t n_rows,
+                      int32_t k, double band, int32_t* sel, uint8_t* flags, int64_t ldf,
+                      double* kth, int32_t* K, int threads) {
+  topk_ctx c = {scores, ld, v, k, band, sel, flags, ldf, kth, K};
+  run_items(n_rows, threads, topk_item, &c);
+}
+
+/* ---- attention ----------------------------------------------------------------
+ * Absorbed-form MLA for one (row, head) over a set of positions S:
+ *   z(s) = sm_scale * sum_{d < D} q(t,h,d) * kv(s,d)       (D = 576)
+ *   p(s) = exp(z(s) - m) / sum_{s'} exp(z(s') - m),  m = max z
+ *   o(t,h,d) = sum_s p(s) * kv(s,d)  for d < Dv (Dv = 512)
+ *   lse(t,h) = m + ln sum_s exp(z(s) - m)
+ * An empty S gives o = 0 and lse = -inf.
+ */
+typedef struct {
+  const oracle_batch* bt;
+  int32_t H, D, Dv;
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* idx; /* [n_rows][k] positions, or NULL for dense */
+  int32_t k;
+  double sm_scale;
+  const int32_t* rows;
+  double* out;
+  double* lse;
+} mla_ctx;
+
+static void mla_item(void* p, int64_t item) {
+  mla_ctx* c = (mla_ctx*)p;
+  int64_t i = item / c->H;
+  int32_t h = (int32_t)(item % c->H);
+  int32_t t = c->rows[i];
+  int32_t b = oracle_row_request(c->bt, t);
+  int64_t v = b < 0 ? 0 : oracle_row_visible(c->bt, t);
+  int32_t D = c->D, Dv = c->Dv;
+  double* o = c->out + (i * c->H + h) * Dv;
+  for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+
+  /* the position list S */
+  int64_t n = 0;
+  int64_t cap = c->idx ? c->k : v;
+  int64_t* S = (int64_t*)malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
+  if (c->idx) {
+    for (int32_t j = 0; j < c->k; ++j) {
+      int32_t s = c->idx[i * c->k + j];
+      if (s >= 0 && s < v) S[n++] = s;
+    }
+  } else {
+    for (int64_t s = 0; s < v; ++s) S[n++] = s;
+  }
+  if (n == 0) {
+    c->lse[i * c->H + h] = -INFINITY;
+    free(S);
+    return;
+  }
+  double* qh = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int d = 0; d < D; ++d)
+    qh[d] = oracle_bf16_decode(c->q[((int64_t)t * c->H + h) * D + d]);
+  double* z = (double*)malloc(sizeof(double) * (size_t)n);
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    const uint16_t* row = c->kv + oracle_slot(c->bt, b, S[j]) * D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += qh[d] * oracle_bf16_decode(row[d]);
+    z[j] = c->sm_scale * dot;
+    if (z[j] > m) m = z[j];
+  }
+  double sum = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    z[j] = exp(z[j] - m);
+    sum += z[j];
+  }
+  for (int64_t j = 0; j < n; ++j) {
+    const uint16_t* row = c->kv + oracle_slot(c->bt, b, S[j]) * D;
+    double pj = z[j] / sum;
+    for (int d = 0; d < Dv; ++d) o[d] += pj * oracle_bf16_decode(row[d]);
+  }
+  c->lse[i * c->H + h] = m + log(sum);
+  free(z);
+  free(qh);
+  free(S);
+}
+
+void oracle_sparse_mla(const oracle_batch* bt, int32_t H, int32_t D, int32_t Dv,
+                       const uint16_t* q, const uint16_t* kv, const int32_t* idx, int32_t k,
+                       double sm_scale, const int32_t* rows, int32_t n_rows, double* out,
+                       double* lse, int threads) {
+  mla_ctx c = {bt, H, D, Dv, q, kv, idx, k, sm_scale, rows, out, lse};
+  run_items((int64_t)n_rows * H, threads, mla_item, &c);
+}
+
+/* Dense MLA: the same attention over every visible position. */
+void oracle_dense_mla(const oracle_batch* bt, int32_t H, int32_t D, int32_t Dv, const uint16_t* q,
+                      const uint16_t* kv, double sm_scale, const int32_t* rows, int32_t n_rows,
+                      double* out, double* lse, int threads) {
+  mla_ctx c = {bt, H, D, Dv, q, kv, NULL, 0, sm_scale, rows, out, lse};
+  run_items((int64_t)n_rows * H, threads, mla_item, &c);
+}
