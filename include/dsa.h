@@ -1,0 +1,212 @@
+/*
+ * dsa.h - C ABI of the DeepSeek Sparse Attention (DSA) decode path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path (DSA bullet of "MTP and sparse attention: NSA and DSA"):
+ *   1. lightning indexer: for query row t and cached token s,
+ *        I(t,s) = sum_h w(t,h) * ReLU(q(t,h) . k(s))
+ *      over 64 heads of 128 dims, FP8 queries and keys with fp32 scales;
+ *   2. top-k: each row keeps its k (= 2048) highest-scoring visible tokens;
+ *   3. absorbed-form MLA over only those tokens: 128 heads score the
+ *      576-wide bf16 latent (512 latent + 64 rope) and average its first 512
+ *      dims, split over KV chunks with an online softmax and merged by
+ *      log-sum-exp (stages 2 and 3 of the sparse decode in "Deepseek
+ *      Details", section DSA).
+ * Batches follow "[SGLang] NSA" (NSAMetadata, init_forward_metadata): a
+ * request has 1 + MTP query rows, its cached length includes them, row j
+ * of a request with n rows and L cached tokens sees the first L - n + 1 + j
+ * tokens, and a page table maps positions to physical 64-token pages.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named in the argument lists are device pointers (HBM), owned
+ *    by the caller, contiguous in the layouts stated; the library never
+ *    allocates or frees on these calls and keeps no pointer after return.
+ *  - Work is enqueued on the given HIP stream(s) (hipStream_t passed as
+ *    void*; NULL = the null stream) and is asynchronous: no call waits for
+ *    the device.  Calls on different streams that share a workspace race.
+ *  - Host scalars are validated; device metadata (cu_seqlens_q, seqlens_k,
+ *    page_table, idx) is trusted to be consistent with them, and kernels
+ *    clamp it so a bad value never reads outside the buffers the host
+ *    scalars describe (bad positions are treated as not visible).
+ *  - Every function returns a dsa_status; on error nothing is enqueued and
+ *    dsa_last_error() returns a message (thread-local).  No exception or
+ *    abort crosses the ABI.
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t); FP8 values
+ *    are OCP e4m3fn codes (uint8_t).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_PAGE_SIZE 64  /* tokens per cache page */
+#define DSA_IDX_HEADS 64  /* indexer heads */
+#define DSA_IDX_DIM 128   /* indexer head dim (FP8) */
+#define DSA_MLA_HEADS 128 /* MLA query heads */
+#define DSA_MLA_DIM 576   /* latent + rope dims of a cached token */
+#define DSA_MLA_DV 512    /* latent dims averaged into the output */
+#define DSA_MAX_TOPK 8192 /* largest k accepted */
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent scalars */
+  DSA_ERR_UNSUPPORTED = 2, /* a shape outside what the kernels implement */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dsa_workspace_size() */
+  DSA_ERR_HIP = 4          /* a HIP launch or event call failed */
+} dsa_status;
+
+/* One batch of requests (host struct; the arrays it points to are on the device).
+ *  batch        B, number of requests (>= 0)
+ *  num_tokens   T = cu_seqlens_q[B], total query rows
+ *  max_q        >= every request's row count
+ *  max_seqlen_k >= every seqlens_k[b]
+ *  max_pages_per_req  row stride of page_table (>= ceil(max_seqlen_k / 64))
+ *  num_pages    physical pages in the caches
+ *  cu_seqlens_q int32 [B+1], cu[0] = 0, non-decreasing; rows of request b
+ *               are cu[b] .. cu[b+1]-1
+ *  seqlens_k    int32 [B], L_b: cached tokens of request b including its
+ *               rows (L_b = 0 marks a padding request: no visible tokens)
+ *  page_table   int32 [B, max_pages_per_req], physical page of logical page
+ *               p of request b; entries past ceil(L_b/64) are never read */
+typedef struct {
+  int32_t batch;
+  int32_t num_tokens;
+  int32_t max_q;
+  int32_t max_seqlen_k;
+  int32_t max_pages_per_req;
+  int32_t num_pages;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  const int32_t* page_table;
+} dsa_batch_t;
+
+/* Lightning-indexer scores ("MTP and sparse attention: NSA and DSA", DSA
+ * bullet; cache layout from the accounting listing: 128 FP8 bytes plus a
+ * 4-byte scale per token).
+ *  q8       uint8 [T, 64, 128]     indexer queries (e4m3fn)
+ *  q_scale  f32 [T]                one positive scale per query row
+ *  w        f32 [T, 64]            per-(row, head) weights (any sign)
+ *  k8_cache uint8 [num_pages, 64, 128]  indexer keys by physical slot
+ *  k_scale  f32 [num_pages, 64]    one positive scale per cached key
+ *  scores   f32 [T, ld] out: scores[t, s] = q_scale[t] * k_scale[slot(s)] *
+ *           sum_h w[t,h] * max(0, sum_d e4m3(q8[t,h,d]) * e4m3(k8[slot(s),d]))
+ *           for s < v_t (row t's visible length); entries s >= v_t are not written.
+ *           With positive scales this equals I(t,s) on the dequantised values.
+ *  ld       >= max_seqlen_k
+ * Errors: INVALID_ARG (null pointers with T > 0, ld too small, bad scalars). */
+int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_scale,
+                    const float* w, const uint8_t* k8_cache, const float* k_scale, float* scores,
+                    int64_t ld, void* stream);
+
+/* Per-row top-k over scores[t, 0 .. v_t) ("MTP and sparse attention: NSA
+ * and DSA", DSA bullet: each query keeps its 2048 highest-scoring tokens).
+ *  scores  f32 [T, ld]; -0.0 ranks as +0.0; NaN ranks above +inf
+ *  k       1 .. DSA_MAX_TOPK
+ *  idx     int32 [T, k] out: the K_t = min(k, v_t) selected logical positions
+ *          (ties at the k-th score go to the lower position), stored in
+ *          idx[t, 0 .. K_t), followed by -1 in idx[t, K_t .. k).  Order within
+ *          the K_t entries: first every position whose score is above the
+ *          threshold bucket, ascending, then the rest, ascending; it is
+ *          deterministic.
+ *  ws      device workspace of >= dsa_workspace_size(DSA_OP_TOPK, ...) bytes
+ * Errors: INVALID_ARG, WORKSPACE. */
+int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse absorbed-MLA decode over selected tokens ("MTP and sparse
+ * attention: NSA and DSA", DSA bullet and per-pair cost; split-KV online
+ * softmax + LSE merge per "Deepseek Details", DSA, stages 2-3).
+ *  q        bf16 [T, 128, 576]       absorbed queries (512 latent + 64 rope)
+ *  kv_cache bf16 [num_pages, 64, 576] latent cache by physical slot
+ *  idx      int32 [T, k]             logical positions; entries < 0 or
+ *           >= v_t are skipped (so -1 padding is allowed); positions must
+ *           be distinct within a row
+ *  sm_scale softmax scale on the 576-dim dot product (1/sqrt(192) for DSA)
+ *  out      bf16 [T, 128, 512] out: softmax(sm_scale * q.kv) @ kv[:, :512],
+ *           rounded to nearest even; zeros for a row with no valid entry
+ *  lse      f32 [T, 128] out (may be NULL): natural-log sum of exp of the
+ *           scaled scores (-inf for a row with no valid entry)
+ *  n_split  KV splits per row (0 = choose), 1 .. 64
+ *  ws       workspace (>= dsa_workspace_size(DSA_OP_SPARSE_MLA, ...))
+ * Errors: INVALID_ARG, WORKSPACE. */
+int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
+                          const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
+                          float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream);
+
+/* Indexer inputs of one layer (device pointers, layouts as dsa_index_score). */
+typedef struct {
+  const uint8_t* q8;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k8_cache;
+  const float* k_scale;
+} dsa_indexer_inputs_t;
+
+/* MLA inputs of one layer (layouts as dsa_sparse_mla_decode). */
+typedef struct {
+  const uint16_t* q;
+  const uint16_t* kv_cache;
+  float sm_scale;
+} dsa_mla_inputs_t;
+
+typedef enum {
+  /* indexer -> top-k -> sparse MLA on the selection just made, on stream_main */
+  DSA_MODE_FUSED = 0,
+  /* Multi-layer Indexer ("Multi-layer Indexer: Overlapping Selection and
+   * Attention in DeepSeek Sparse Attention", abstract): the attention reads
+   * the previous indexer layer's selection (opts->attend_idx) on stream_main
+   * while this call's indexer + top-k run concurrently on stream_aux and
+   * write idx_out (the selection the next layer attends).  stream_main
+   * waits for stream_aux before the call's work counts as done. */
+  DSA_MODE_MLI = 1
+} dsa_step_mode;
+
+typedef struct {
+  int32_t mode;               /* dsa_step_mode */
+  int32_t n_split;            /* as dsa_sparse_mla_decode (0 = choose) */
+  const int32_t* attend_idx;  /* MLI: int32 [T, k] selection the attention reads */
+} dsa_step_opts_t;
+
+/* One decode step of one layer: indexer scores, top-k, sparse MLA.
+ *  ix, mla   this layer's inputs
+ *  k         tokens kept per row
+ *  idx_out   int32 [T, k] out: the selection of ix (as dsa_topk)
+ *  out, lse  as dsa_sparse_mla_decode; attention over idx_out (FUSED) or
+ *            over opts->attend_idx (MLI)
+ *  ws        >= dsa_workspace_size(DSA_OP_DECODE_STEP, ...) bytes
+ *  stream_main, stream_aux  stream_aux is used only in MLI mode (must be
+ *            non-NULL and differ from stream_main there)
+ * Errors: INVALID_ARG, WORKSPACE, HIP. */
+int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
+                    const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
+                    int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream_main, void* stream_aux);
+
+typedef enum {
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_MLA = 2,
+  DSA_OP_DECODE_STEP = 3
+} dsa_op;
+
+/* Workspace bytes an op needs for this batch, k and n_split (0 = the
+ * library's choice, as in the calls).  0 for an invalid request. */
+size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n_split);
+
+/* KV splits the library chooses for a batch when n_split = 0. */
+int32_t dsa_default_splits(const dsa_batch_t* batch, int32_t k);
+
+const char* dsa_status_string(int status);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,9 @@
+"""DSA decode hot path for MI355X (gfx950): lightning indexer, top-k and
+sparse absorbed-MLA decode behind a C ABI (include/dsa.h, libdsa.so).
+
+The Python names mirror the C entry points and only marshal arguments.
+"""
+from .binding import (  # noqa: F401
+    DSA_MODE_FUSED, DSA_MODE_MLI, DSA_OP_DECODE_STEP, DSA_OP_SPARSE_MLA, DSA_OP_TOPK, EXPORTS,
+    Batch, DsaError, dsa_decode_step, dsa_default_splits, dsa_index_score, dsa_sparse_mla_decode,
+    dsa_topk, dsa_workspace_size, lib)

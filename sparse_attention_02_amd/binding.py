@@ -1,0 +1,170 @@
+"""ctypes binding of libdsa.so (the C ABI declared in include/dsa.h).
+
+Argument marshalling only: tensors are passed as device pointers
+(torch.Tensor.data_ptr()) and streams as HIP stream handles.  Every step of
+the path runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP = 1, 2, 3
+DSA_MODE_FUSED, DSA_MODE_MLI = 0, 1
+PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 128, 128, 576, 512, 8192
+
+EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
+           "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class dsa_batch_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("max_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+                ("max_pages_per_req", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("cu_seqlens_q", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p)]
+
+
+class dsa_indexer_inputs_t(ctypes.Structure):
+    _fields_ = [("q8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("k8_cache", ctypes.c_void_p), ("k_scale", ctypes.c_void_p)]
+
+
+class dsa_mla_inputs_t(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("kv_cache", ctypes.c_void_p),
+                ("sm_scale", ctypes.c_float)]
+
+
+class dsa_step_opts_t(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_split", ctypes.c_int32),
+                ("attend_idx", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                 ctypes.c_float)
+        bp = ctypes.POINTER(dsa_batch_t)
+        L.dsa_index_score.argtypes = [bp, vp, vp, vp, vp, vp, vp, i64, vp]
+        L.dsa_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
+        L.dsa_sparse_mla_decode.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
+        L.dsa_decode_step.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
+                                      ctypes.POINTER(dsa_mla_inputs_t), i32,
+                                      ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp, sz, vp, vp]
+        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
+        L.dsa_workspace_size.restype = sz
+        L.dsa_default_splits.argtypes = [bp, i32]
+        L.dsa_default_splits.restype = i32
+        L.dsa_status_string.argtypes = [ctypes.c_int]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_last_error.argtypes = []
+        L.dsa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(rc: int):
+    if rc != DSA_OK:
+        msg = lib().dsa_last_error().decode() or lib().dsa_status_string(rc).decode()
+        raise DsaError(rc, msg)
+
+
+class Batch:
+    """Batch metadata on the device plus its host scalars (dsa_batch_t)."""
+
+    def __init__(self, cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor,
+                 page_table: torch.Tensor, num_pages: int, max_q: int, max_seqlen_k: int):
+        self.cu_seqlens_q = cu_seqlens_q
+        self.seqlens_k = seqlens_k
+        self.page_table = page_table
+        B = int(seqlens_k.shape[0])
+        T = int(cu_seqlens_q[-1].item()) if B else 0
+        self.c = dsa_batch_t(B, T, int(max_q), int(max_seqlen_k),
+                             int(page_table.shape[1]) if page_table.dim() == 2 else 0,
+                             int(num_pages), _ptr(cu_seqlens_q), _ptr(seqlens_k),
+                             _ptr(page_table))
+
+    @property
+    def T(self) -> int:
+        return int(self.c.num_tokens)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def dsa_workspace_size(op: int, batch: Batch, k: int, n_split: int = 0) -> int:
+    return int(lib().dsa_workspace_size(op, batch.ref(), k, n_split))
+
+
+def dsa_default_splits(batch: Batch, k: int) -> int:
+    return int(lib().dsa_default_splits(batch.ref(), k))
+
+
+def dsa_index_score(batch: Batch, q8, q_scale, w, k8_cache, k_scale, scores, ld: int,
+                    stream=None):
+    _check(lib().dsa_index_score(batch.ref(), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8_cache),
+                                 _ptr(k_scale), _ptr(scores), int(ld), _stream(stream)))
+
+
+def dsa_topk(batch: Batch, scores, ld: int, k: int, idx, ws, ws_bytes: int, stream=None):
+    _check(lib().dsa_topk(batch.ref(), _ptr(scores), int(ld), int(k), _ptr(idx), _ptr(ws),
+                          int(ws_bytes), _stream(stream)))
+
+
+def dsa_sparse_mla_decode(batch: Batch, q, kv_cache, idx, k: int, sm_scale: float, out, lse,
+                          n_split: int, ws, ws_bytes: int, stream=None):
+    _check(lib().dsa_sparse_mla_decode(batch.ref(), _ptr(q), _ptr(kv_cache), _ptr(idx), int(k),
+                                       float(sm_scale), _ptr(out), _ptr(lse), int(n_split),
+                                       _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def dsa_decode_step(batch: Batch, ix: dict, mla: dict, k: int, mode: int, n_split: int,
+                    attend_idx, idx_out, out, lse, ws, ws_bytes: int, stream_main=None,
+                    stream_aux=None):
+    """ix: q8, q_scale, w, k8_cache, k_scale; mla: q, kv_cache, sm_scale."""
+    ixs = dsa_indexer_inputs_t(_ptr(ix["q8"]), _ptr(ix["q_scale"]), _ptr(ix["w"]),
+                               _ptr(ix["k8_cache"]), _ptr(ix["k_scale"]))
+    ms = dsa_mla_inputs_t(_ptr(mla["q"]), _ptr(mla["kv_cache"]), float(mla["sm_scale"]))
+    opts = dsa_step_opts_t(int(mode), int(n_split), _ptr(attend_idx))
+    aux = None if stream_aux is None else _stream(stream_aux)
+    _check(lib().dsa_decode_step(batch.ref(), ctypes.byref(ixs), ctypes.byref(ms), int(k),
+                                 ctypes.byref(opts), _ptr(idx_out), _ptr(out), _ptr(lse),
+                                 _ptr(ws), int(ws_bytes), _stream(stream_main), aux))

@@ -1,0 +1,269 @@
+// C ABI of the DSA decode path: host-side validation, workspace carve-up and
+// stream orchestration.  All arithmetic runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <string>
+
+#include "dsa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return DSA_ERR_HIP;
+}
+
+using dsa::align_up;
+using dsa::BatchArgs;
+
+// host scalars of the batch
+int check_batch(const dsa_batch_t* b) {
+  if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->batch < 0 || b->num_tokens < 0 || b->max_q < 0 || b->max_seqlen_k < 0 ||
+      b->max_pages_per_req < 0 || b->num_pages < 0)
+    return fail(DSA_ERR_INVALID_ARG, "negative batch scalar");
+  if (b->batch > 0 && (!b->cu_seqlens_q || !b->seqlens_k))
+    return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_q / seqlens_k is NULL");
+  if (b->batch == 0 && b->num_tokens != 0)
+    return fail(DSA_ERR_INVALID_ARG, "num_tokens > 0 with no requests");
+  if (b->num_tokens > 0 && (b->max_q < 1 || b->max_q > b->num_tokens))
+    return fail(DSA_ERR_INVALID_ARG, "max_q must be in [1, num_tokens]");
+  if (b->max_seqlen_k > 0) {
+    if (!b->page_table) return fail(DSA_ERR_INVALID_ARG, "page_table is NULL");
+    if ((int64_t)b->max_pages_per_req * DSA_PAGE_SIZE < b->max_seqlen_k)
+      return fail(DSA_ERR_INVALID_ARG, "max_pages_per_req * 64 < max_seqlen_k");
+    if (b->num_pages < 1) return fail(DSA_ERR_INVALID_ARG, "num_pages < 1");
+  }
+  return DSA_OK;
+}
+
+int64_t step_ld(const dsa_batch_t* b) { return (int64_t)align_up((size_t)b->max_seqlen_k, 64); }
+
+struct StepWs {
+  size_t scores_off, topk_off, mla_off, total;
+};
+
+StepWs step_layout(const dsa_batch_t* b, int used_splits) {
+  const BatchArgs a = dsa::batch_args(*b);
+  StepWs w;
+  size_t off = 0;
+  w.scores_off = off;
+  off = align_up(off + (size_t)b->num_tokens * (size_t)step_ld(b) * 4, 256);
+  w.topk_off = off;
+  off = align_up(off + dsa::topk_ws_layout(a).total, 256);
+  w.mla_off = off;
+  off = align_up(off + dsa::mla_ws_layout(a, used_splits).total, 256);
+  w.total = off;
+  return w;
+}
+
+int resolve_splits(const dsa_batch_t* b, int32_t k, int32_t n_split, int* used) {
+  if (n_split < 0 || n_split > dsa::kMaxSplits)
+    return fail(DSA_ERR_INVALID_ARG, "n_split must be in [0, 64]");
+  const int ns = n_split == 0 ? dsa::default_splits(dsa::batch_args(*b), k) : n_split;
+  *used = dsa::mla_splits_used(k, ns);
+  return DSA_OK;
+}
+
+// two events per thread and device for the cross-stream joins of MLI mode
+struct EventPair {
+  int device = -1;
+  hipEvent_t start = nullptr, done = nullptr;
+};
+thread_local EventPair g_events;
+
+int get_events(hipEvent_t* start, hipEvent_t* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (g_events.device != dev) {
+    hipEvent_t a = nullptr, c = nullptr;
+    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    e = hipEventCreateWithFlags(&c, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return hip_fail(e, "hipEventCreateWithFlags");
+    }
+    // events of another device are left alive: they may still be pending
+    g_events.device = dev;
+    g_events.start = a;
+    g_events.done = c;
+  }
+  *start = g_events.start;
+  *done = g_events.done;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int32_t dsa_default_splits(const dsa_batch_t* batch, int32_t k) {
+  if (check_batch(batch) != DSA_OK || k < 1) return 1;
+  return dsa::default_splits(dsa::batch_args(*batch), k);
+}
+
+size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n_split) {
+  if (check_batch(batch) != DSA_OK || k < 1 || k > DSA_MAX_TOPK) return 0;
+  const BatchArgs a = dsa::batch_args(*batch);
+  int used = 1;
+  switch (op) {
+    case DSA_OP_TOPK:
+      return dsa::topk_ws_layout(a).total;
+    case DSA_OP_SPARSE_MLA:
+      if (resolve_splits(batch, k, n_split, &used) != DSA_OK) return 0;
+      return dsa::mla_ws_layout(a, used).total;
+    case DSA_OP_DECODE_STEP:
+      if (resolve_splits(batch, k, n_split, &used) != DSA_OK) return 0;
+      return step_layout(batch, used).total;
+    default:
+      return 0;
+  }
+}
+
+int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_scale,
+                    const float* w, const uint8_t* k8_cache, const float* k_scale, float* scores,
+                    int64_t ld, void* stream) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (ld < batch->max_seqlen_k) return fail(DSA_ERR_INVALID_ARG, "ld < max_seqlen_k");
+  if (batch->num_tokens == 0 || batch->max_seqlen_k == 0) return DSA_OK;
+  if (!q8 || !q_scale || !w || !k8_cache || !k_scale || !scores)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = dsa::launch_index_score(dsa::batch_args(*batch), q8, q_scale, w, k8_cache,
+                                         k_scale, scores, ld, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "index_score launch");
+}
+
+int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
+             void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  if (ld < batch->max_seqlen_k) return fail(DSA_ERR_INVALID_ARG, "ld < max_seqlen_k");
+  if (batch->num_tokens == 0) return DSA_OK;
+  if (!idx || (!scores && batch->max_seqlen_k > 0))
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const size_t need = dsa::topk_ws_layout(dsa::batch_args(*batch)).total;
+  if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "top-k workspace too small");
+  hipError_t e = dsa::launch_topk(dsa::batch_args(*batch), scores, ld, k, idx, ws,
+                                  (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");
+}
+
+int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
+                          const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
+                          float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  int used = 1;
+  rc = resolve_splits(batch, k, n_split, &used);
+  if (rc) return rc;
+  if (batch->num_tokens == 0) return DSA_OK;
+  if (!q || !idx || !out || (!kv_cache && batch->max_seqlen_k > 0))
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const dsa::BatchArgs a = dsa::batch_args(*batch);
+  const size_t need = dsa::mla_ws_layout(a, used).total;
+  if (need > 0 && (ws_bytes < need || !ws))
+    return fail(DSA_ERR_WORKSPACE, "attention workspace too small");
+  hipError_t e = dsa::launch_sparse_mla(a, q, kv_cache, idx, k, sm_scale, out, lse, used, ws,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA launch");
+}
+
+int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
+                    const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
+                    int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream_main, void* stream_aux) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (!ix || !mla || !opts) return fail(DSA_ERR_INVALID_ARG, "NULL argument struct");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  if (opts->mode != DSA_MODE_FUSED && opts->mode != DSA_MODE_MLI)
+    return fail(DSA_ERR_INVALID_ARG, "unknown mode");
+  const bool mli = opts->mode == DSA_MODE_MLI;
+  if (mli && (!opts->attend_idx || !stream_aux || stream_aux == stream_main))
+    return fail(DSA_ERR_INVALID_ARG, "MLI mode needs attend_idx and a second stream");
+  int used = 1;
+  rc = resolve_splits(batch, k, opts->n_split, &used);
+  if (rc) return rc;
+  if (batch->num_tokens == 0) return DSA_OK;
+  if (!idx_out || !out || !mla->q || !ix->q8 || !ix->q_scale || !ix->w ||
+      (batch->max_seqlen_k > 0 && (!ix->k8_cache || !ix->k_scale || !mla->kv_cache)))
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const StepWs L = step_layout(batch, used);
+  if (ws_bytes < L.total || !ws) return fail(DSA_ERR_WORKSPACE, "step workspace too small");
+  const BatchArgs a = dsa::batch_args(*batch);
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + L.scores_off);
+  void* topk_ws = base + L.topk_off;
+  void* mla_ws = base + L.mla_off;
+  const int64_t ld = step_ld(batch);
+  hipStream_t sm = (hipStream_t)stream_main;
+
+  if (!mli) {
+    hipError_t e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache,
+                                           ix->k_scale, scores, ld, sm);
+    if (e != hipSuccess) return hip_fail(e, "index_score launch");
+    e = dsa::launch_topk(a, scores, ld, k, idx_out, topk_ws, sm);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, idx_out, k, mla->sm_scale, out, lse,
+                               used, mla_ws, sm);
+    if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+    return DSA_OK;
+  }
+
+  // MLI: attention over the previous indexer layer's selection on the main
+  // stream, this layer's indexer + top-k on the aux stream, joined at the end
+  hipStream_t sa = (hipStream_t)stream_aux;
+  hipEvent_t ev_start, ev_done;
+  rc = get_events(&ev_start, &ev_done);
+  if (rc) return rc;
+  hipError_t e = hipEventRecord(ev_start, sm);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = hipStreamWaitEvent(sa, ev_start, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
+                              ld, sa);
+  if (e != hipSuccess) return hip_fail(e, "index_score launch");
+  e = dsa::launch_topk(a, scores, ld, k, idx_out, topk_ws, sa);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, opts->attend_idx, k, mla->sm_scale, out,
+                             lse, used, mla_ws, sm);
+  if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+  e = hipEventRecord(ev_done, sa);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = hipStreamWaitEvent(sm, ev_done, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// Device view of the batch metadata; host scalars copied by value.
+struct BatchArgs {
+  int32_t B, T, max_q, max_seqlen_k, max_pages, num_pages;
+  const int32_t* cu;     // [B+1]
+  const int32_t* lens;   // [B]
+  const int32_t* pages;  // [B, max_pages]
+};
+
+inline BatchArgs batch_args(const dsa_batch_t& b) {
+  return BatchArgs{b.batch,        b.num_tokens,   b.max_q,     b.max_seqlen_k,
+                   b.max_pages_per_req, b.num_pages, b.cu_seqlens_q, b.seqlens_k,
+                   b.page_table};
+}
+
+constexpr int kTopkBins = 2048;      // first radix digit: key bits 31..21
+constexpr int kTopkSeg = 8192;       // scores per histogram / collect work-group
+constexpr int kMlaTile = 32;         // selected tokens per attention tile
+constexpr int kMaxSplits = 64;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace carve-up of the top-k (all sizes in bytes).
+struct TopkWs {
+  size_t hist_off, ctrl_off, cand_off, total;
+};
+TopkWs topk_ws_layout(const BatchArgs& b);
+
+struct MlaWs {
+  size_t opart_off, lpart_off, total;
+};
+MlaWs mla_ws_layout(const BatchArgs& b, int n_split);
+
+int default_splits(const BatchArgs& b, int k);
+
+// KV splits actually launched for k tokens per row and a requested split count.
+int mla_splits_used(int k, int n_split);
+
+hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float* q_scale,
+                              const float* w, const uint8_t* k8, const float* k_scale,
+                              float* scores, int64_t ld, hipStream_t s);
+
+hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
+                       void* ws, hipStream_t s);
+
+hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
+                             const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,
+                             int n_split, void* ws, hipStream_t s);
+
+}  // namespace dsa

@@ -306,13 +306,21 @@ static void k_range(void* p, int64_t lo, int64_t hi) {
     while (b + 1 < c->B && c->key_off[b + 1] <= g) ++b;
     int64_t s = g - c->key_off[b];
     double amax = 0.0;
-    for (int d = 0; d < c->D; ++d) {
-      double v = normal(c->key_base, (uint64_t)(g * c->D + d));
-      if (c->heavy && c->heavy[g]) v += c->heavy_gain * c->dir[(int64_t)b * c->D + d];
-      if (c->noise_scale != 0.0) v += c->noise_scale * normal(c->key_noise, (uint64_t)(g * c->D + d));
-      buf[d] = v;
-      if (fabs(v) > amax) amax = fabs(v);
+    /* D is even, so the key's normals are whole Box-Muller pairs */
+    for (int d = 0; d < c->D; d += 2)
+      normal_pair(c->key_base, (uint64_t)(g * c->D + d) >> 1, &buf[d], &buf[d + 1]);
+    if (c->heavy && c->heavy[g])
+      for (int d = 0; d < c->D; ++d) buf[d] += c->heavy_gain * c->dir[(int64_t)b * c->D + d];
+    if (c->noise_scale != 0.0) {
+      for (int d = 0; d < c->D; d += 2) {
+        double e0, e1;
+        normal_pair(c->key_noise, (uint64_t)(g * c->D + d) >> 1, &e0, &e1);
+        buf[d] += c->noise_scale * e0;
+        buf[d + 1] += c->noise_scale * e1;
+      }
     }
+    for (int d = 0; d < c->D; ++d)
+      if (fabs(buf[d]) > amax) amax = fabs(buf[d]);
     float sc = amax > 0 ? (float)(amax / 448.0) : 1.0f;
     int64_t page = c->page_table[(int64_t)b * c->max_pages + s / c->P];
     int64_t slot = page * c->P + s % c->P;

@@ -193,13 +193,15 @@ def make_batch(n_q, L, *, seed: int, paging: str = "identity", heavy=64, layers:
     B = max(len(n_q), len(L))
     n_q = np.broadcast_to(n_q, (B,)).astype(np.int32)
     L = np.broadcast_to(L, (B,)).astype(np.int32)
-    if np.any(L < n_q):
+    if np.any((L < n_q) & (L != 0)):
+        # L = 0 is a padding request (no visible tokens); otherwise the
+        # cache holds the request's new rows
         raise ValueError("each request's cache must hold its new rows")
     cu = np.zeros(B + 1, np.int32)
     cu[1:] = np.cumsum(n_q)
     T = int(cu[-1])
     pages_per = (L.astype(np.int64) + PAGE - 1) // PAGE
-    num_pages = int(pages_per.sum()) + pool_extra_pages
+    num_pages = max(int(pages_per.sum()) + pool_extra_pages, 1)
     max_pages = max(int(pages_per.max()) if B else 1, 1)
     pool = (permutation(seed, S_PERM, num_pages) if paging == "shuffled"
             else np.arange(num_pages, dtype=np.int32))

@@ -1,0 +1,142 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/dsa.h declares, and rejects bad host arguments before it touches
+the device (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_02_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B._LIB_PATH):
+        from sparse_attention_02_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    d = _declared()
+    for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step"):
+        assert name in d
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(B.EXPORTS) == _declared()
+
+
+def _batch(B_=2, T=4, max_q=2, max_seqlen_k=300, max_pages=5, num_pages=10, ptrs=True):
+    fake = 0x1000 if ptrs else None
+    return B.dsa_batch_t(B_, T, max_q, max_seqlen_k, max_pages, num_pages, fake, fake, fake)
+
+
+def _err(L):
+    return L.dsa_last_error().decode()
+
+
+def test_status_strings(L):
+    assert L.dsa_status_string(0) == b"ok"
+    assert L.dsa_status_string(3) == b"workspace too small"
+
+
+def test_batch_validation(L):
+    P = 0x1000
+    rc = L.dsa_topk(None, P, 300, 16, P, P, 1 << 30, None)
+    assert rc == B.DSA_ERR_INVALID_ARG and "batch" in _err(L)
+    b = _batch(max_pages=4)  # 4 * 64 < 300
+    assert L.dsa_topk(ctypes.byref(b), P, 300, 16, P, P, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    b = _batch(max_q=5)  # max_q > T
+    assert L.dsa_topk(ctypes.byref(b), P, 300, 16, P, P, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    b = _batch(ptrs=False)
+    assert L.dsa_topk(ctypes.byref(b), P, 300, 16, P, P, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+
+
+def test_topk_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    for k in (0, -3, 8193):
+        assert L.dsa_topk(ctypes.byref(b), P, 300, k, P, P, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(ctypes.byref(b), P, 299, 16, P, P, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    need = L.dsa_workspace_size(B.DSA_OP_TOPK, ctypes.byref(b), 16, 0)
+    assert need > 0
+    rc = L.dsa_topk(ctypes.byref(b), P, 300, 16, P, P, need - 1, None)
+    assert rc == B.DSA_ERR_WORKSPACE
+    assert L.dsa_topk(ctypes.byref(b), P, 300, 16, None, P, need, None) == B.DSA_ERR_INVALID_ARG
+
+
+def test_index_score_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    assert L.dsa_index_score(ctypes.byref(b), P, P, P, P, P, P, 10, None) == B.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_score(ctypes.byref(b), None, P, P, P, P, P, 300, None) == \
+        B.DSA_ERR_INVALID_ARG
+
+
+def test_sparse_mla_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    assert L.dsa_sparse_mla_decode(ctypes.byref(b), P, P, P, 16, 0.1, P, None, 65, P, 1 << 30,
+                                   None) == B.DSA_ERR_INVALID_ARG
+    need = L.dsa_workspace_size(B.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 4)
+    assert need >= 4 * 4 * 128 * 512 * 4
+    assert L.dsa_sparse_mla_decode(ctypes.byref(b), P, P, P, 2048, 0.1, P, None, 4, P, need - 1,
+                                   None) == B.DSA_ERR_WORKSPACE
+    # a single split needs no workspace
+    assert L.dsa_workspace_size(B.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 1) == 0
+
+
+def test_decode_step_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    ix = B.dsa_indexer_inputs_t(P, P, P, P, P)
+    ml = B.dsa_mla_inputs_t(P, P, 0.07)
+    need = L.dsa_workspace_size(B.DSA_OP_DECODE_STEP, ctypes.byref(b), 64, 0)
+    bad_mode = B.dsa_step_opts_t(7, 0, None)
+    assert L.dsa_decode_step(ctypes.byref(b), ctypes.byref(ix), ctypes.byref(ml), 64,
+                             ctypes.byref(bad_mode), P, P, None, P, need, None, None) == \
+        B.DSA_ERR_INVALID_ARG
+    mli = B.dsa_step_opts_t(B.DSA_MODE_MLI, 0, None)  # no attend_idx
+    assert L.dsa_decode_step(ctypes.byref(b), ctypes.byref(ix), ctypes.byref(ml), 64,
+                             ctypes.byref(mli), P, P, None, P, need, None, 0x2000) == \
+        B.DSA_ERR_INVALID_ARG
+    mli = B.dsa_step_opts_t(B.DSA_MODE_MLI, 0, P)
+    assert L.dsa_decode_step(ctypes.byref(b), ctypes.byref(ix), ctypes.byref(ml), 64,
+                             ctypes.byref(mli), P, P, None, P, need, 0x2000, 0x2000) == \
+        B.DSA_ERR_INVALID_ARG  # same stream twice
+    fused = B.dsa_step_opts_t(B.DSA_MODE_FUSED, 0, None)
+    assert L.dsa_decode_step(ctypes.byref(b), ctypes.byref(ix), ctypes.byref(ml), 64,
+                             ctypes.byref(fused), P, P, None, P, need - 1, None, None) == \
+        B.DSA_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op(L):
+    b = B.dsa_batch_t(0, 0, 0, 0, 0, 0, None, None, None)
+    assert L.dsa_topk(ctypes.byref(b), None, 0, 16, None, None, 0, None) == B.DSA_OK
+    assert L.dsa_sparse_mla_decode(ctypes.byref(b), None, None, None, 16, 0.1, None, None, 0,
+                                   None, 0, None) == B.DSA_OK
+    assert L.dsa_index_score(ctypes.byref(b), None, None, None, None, None, None, 0, None) == \
+        B.DSA_OK
+
+
+def test_workspace_sizes_grow_with_the_batch(L):
+    small = _batch(T=4, max_seqlen_k=300)
+    big = _batch(T=4, max_seqlen_k=600, max_pages=10)
+    for op in (B.DSA_OP_TOPK, B.DSA_OP_DECODE_STEP):
+        assert L.dsa_workspace_size(op, ctypes.byref(big), 64, 0) > \
+            L.dsa_workspace_size(op, ctypes.byref(small), 64, 0)
+    assert L.dsa_workspace_size(99, ctypes.byref(small), 64, 0) == 0
+    assert L.dsa_default_splits(ctypes.byref(small), 2048) == 64

@@ -1,0 +1,284 @@
+"""Parity of the HIP path with the float64 oracle, through the C ABI.
+
+Small cases span several tiles and ragged tails (L around the 64-token page
+and the 2048-token selection, 1-5 rows per request, padding requests);
+the five workloads run at their full sizes with the launch configuration
+the bench uses, checked on sampled rows.  The bars:
+  * scores: within SCORE_RTOL of the row's largest float64 score;
+  * selection: identical to the oracle's outside its flagged tie band
+    (bit-exact when both sides rank the same float32 scores);
+  * attention: bf16 output within max-abs 2e-2 and mean-abs 2e-3 (also
+    relative to the reference rms), lse within 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (K, O, bf16_to_f64, check_attention, check_scores, check_selection,
+                        decode_step, dsa, index_scores, oracle_rows, sparse_mla, synth, sync,
+                        to_device, topk)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    dict(n_q=[1], L=[1]),
+    dict(n_q=[1], L=[63]),
+    dict(n_q=[2, 1], L=[64, 65]),
+    dict(n_q=[3, 1, 2], L=[2047, 2048, 2049]),
+    dict(n_q=[2, 2, 1, 5], L=[130, 5000, 0, 4100]),
+    dict(n_q=[1, 2], L=[9000, 20000]),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.lib()
+
+
+def _small(case, seed, paging="shuffled", mla_scale=None, heavy=16):
+    kw = {} if mla_scale is None else dict(mla_scale=mla_scale)
+    return synth.make_batch(case["n_q"], case["L"], seed=seed, paging=paging, heavy=heavy,
+                            pool_extra_pages=3, **kw)
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+def test_index_score_small(ci):
+    b = _small(SMALL[ci], 100 + ci)
+    d = to_device(b)
+    scores, ld = index_scores(d)
+    sync()
+    rows = list(range(b.T))
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, rows)
+    check_scores(scores.cpu().numpy().astype(np.float64), sc, vis)
+    # positions past a row's visible length are not written
+    g = scores.cpu().numpy()
+    for i, v in enumerate(vis):
+        assert np.isnan(g[i, v:]).all()
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+@pytest.mark.parametrize("k", [1, 37, 2048])
+def test_topk_small_exact_on_same_scores(ci, k):
+    """Given identical float32 scores the GPU selection equals the oracle's exactly."""
+    b = _small(SMALL[ci], 200 + ci)
+    d = to_device(b)
+    scores, ld = index_scores(d)
+    idx = topk(d, scores, ld, k)
+    sync()
+    s64 = scores.cpu().numpy().astype(np.float64)
+    vis = b.visible()
+    sel, flags, kth, Ks = O.topk(np.nan_to_num(s64, nan=-np.inf), vis, k, band=0.0)
+    g = idx.cpu().numpy()
+    for i in range(b.T):
+        K_ = int(Ks[i])
+        assert sorted(g[i, :K_].tolist()) == g[i, :K_].tolist()  # ascending
+        assert set(g[i, :K_].tolist()) == set(sel[i, :K_].tolist()), i
+        assert (g[i, K_:] == -1).all()
+
+
+@pytest.mark.parametrize("pattern", ["all_equal", "few_values", "negative", "signed_zero",
+                                     "heavy_ties"])
+def test_topk_adversarial_scores(pattern):
+    rng = np.random.default_rng(7)
+    b = _small(dict(n_q=[1, 2, 1], L=[30000, 12000, 3000]), 300, heavy=0)
+    d = to_device(b)
+    T, ld = b.T, 30016
+    vis = b.visible()
+    if pattern == "all_equal":
+        s = np.full((T, ld), 1.5, np.float32)
+    elif pattern == "few_values":
+        s = rng.integers(0, 5, (T, ld)).astype(np.float32)
+    elif pattern == "negative":
+        s = -np.abs(rng.normal(size=(T, ld))).astype(np.float32)
+    elif pattern == "signed_zero":
+        s = np.where(rng.random((T, ld)) < 0.5, np.float32(-0.0), np.float32(0.0))
+        s[:, ::97] = 1.0
+    else:
+        s = np.round(rng.normal(size=(T, ld)), 1).astype(np.float32)
+    for k in (1, 2048, 5000):
+        idx = topk(d, torch.from_numpy(s).cuda(), ld, k)
+        sync()
+        sel, _, _, Ks = O.topk(s.astype(np.float64), vis, k, band=0.0)
+        g = idx.cpu().numpy()
+        for i in range(T):
+            K_ = int(Ks[i])
+            assert set(g[i, :K_].tolist()) == set(sel[i, :K_].tolist()), (pattern, k, i)
+            assert (g[i, K_:] == -1).all()
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+def test_selection_end_to_end_small(ci):
+    b = _small(SMALL[ci], 400 + ci)
+    d = to_device(b)
+    scores, ld = index_scores(d)
+    idx = topk(d, scores, ld)
+    sync()
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, list(range(b.T)))
+    check_selection(idx.cpu().numpy(), sel, flags, Ks)
+
+
+@pytest.mark.parametrize("ci", [0, 2, 3, 4, 5])
+@pytest.mark.parametrize("n_split", [1, 2, 7])
+@pytest.mark.parametrize("stress", [False, True])
+def test_sparse_mla_small_oracle_selection(ci, n_split, stress):
+    """Attention fed the oracle's selection, for several split counts;
+    `stress` draws q and kv from N(0,1) so the absolute bound bites."""
+    b = _small(SMALL[ci], 500 + ci, mla_scale=1.0 if stress else None)
+    d = to_device(b)
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, list(range(b.T)))
+    idx = torch.from_numpy(sel).cuda()
+    out, lse = sparse_mla(d, idx, n_split=n_split)
+    sync()
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], sel, list(range(b.T)), synth.SM_SCALE)
+    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse)
+
+
+def test_sparse_mla_split_invariance_and_determinism():
+    b = _small(SMALL[5], 600, mla_scale=1.0)
+    d = to_device(b)
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, list(range(b.T)))
+    idx = torch.from_numpy(sel).cuda()
+    o1, l1 = sparse_mla(d, idx, n_split=1)
+    o4, l4 = sparse_mla(d, idx, n_split=4)
+    o4b, l4b = sparse_mla(d, idx, n_split=4)
+    sync()
+    assert torch.equal(o4, o4b) and torch.equal(l4, l4b)
+    # the split count changes only fp32 rounding before the final bf16
+    # rounding: at most one bf16 ulp apart (2^-7 relative covers 1-2 ulps)
+    a, c = o1.float(), o4.float()
+    assert ((a - c).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), c.abs()) + 1e-6).all()
+    assert (l1 - l4).abs().max().item() <= 1e-4
+
+
+def test_sparse_mla_handles_unsorted_padded_and_invalid_positions():
+    b = _small(dict(n_q=[2], L=[3000]), 700, mla_scale=1.0)
+    d = to_device(b)
+    rng = np.random.default_rng(1)
+    sel = np.full((2, 256), -1, np.int32)
+    pos = rng.choice(2999, 150, replace=False).astype(np.int32)
+    sel[:, :150] = pos
+    sel[0, 150] = 2999  # not visible to row 0: skipped
+    sel[1, 150] = 2999
+    sel[:, 151] = 5000  # past the cache: skipped
+    rng.shuffle(sel[1])
+    out, lse = sparse_mla(d, torch.from_numpy(sel).cuda(), k=256, n_split=3)
+    sync()
+    meta = O.Meta.of(b)
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], sel, [0, 1], synth.SM_SCALE)
+    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse)
+
+
+def test_page_permutation_invariance_bitwise():
+    case = dict(n_q=[2, 1], L=[5000, 3000])
+    b = _small(case, 800, paging="identity")
+    d = to_device(b)
+    idx1, out1, lse1 = decode_step(d)
+    # same logical data, physical pages permuted
+    perm = np.random.default_rng(3).permutation(b.num_pages).astype(np.int32)
+    b2 = _small(case, 800, paging="identity")
+    for lst in (b2.k8, b2.k_scale, b2.kv):
+        x = lst[0].copy()
+        lst[0][perm] = x
+    b2.page_table = perm[b.page_table]
+    d2 = to_device(b2)
+    idx2, out2, lse2 = decode_step(d2)
+    sync()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+def test_decode_step_small(ci):
+    b = _small(SMALL[ci], 900 + ci, mla_scale=1.0)
+    d = to_device(b)
+    idx, out, lse = decode_step(d)
+    idx2, out2, lse2 = decode_step(d)
+    sync()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2)  # deterministic
+    rows = list(range(b.T))
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, rows)
+    g = idx.cpu().numpy()
+    check_selection(g, sel, flags, Ks)
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], g, rows, synth.SM_SCALE)
+    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse)
+
+
+# ------------------------------------------------------------ full workloads
+
+_cache = {}
+
+
+def _workload(i):
+    if i not in _cache:
+        _cache.clear()
+        b = synth.make_workload(i)
+        _cache[i] = (b, to_device(b))
+    return _cache[i]
+
+
+def _sample_rows(T, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1}
+    rows.update(rng.choice(T, min(n, T), replace=False).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("wi", [0, 1, 2, 3])
+def test_workload_decode_step(wi):
+    b, d = _workload(wi)
+    print(f"workload {wi} {b.name}: T={b.T} pages={b.num_pages}", flush=True)
+    idx, out, lse = decode_step(d)
+    sync()
+    rows = list(range(b.T)) if wi == 0 else _sample_rows(b.T, 6, wi)
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, rows)
+    g = idx[rows].cpu().numpy()
+    check_selection(g, sel, flags, Ks)
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], g, rows, synth.SM_SCALE)
+    # the oracle over the GPU's selection, per row
+    gi = np.zeros((len(rows), K), np.int32)
+    gi[:] = g
+    check_attention(bf16_to_f64(out[rows]), ref, lse[rows].cpu().numpy(), ref_lse)
+    # heavy tokens are always selected
+    for j, t in enumerate(rows):
+        bi = int(np.searchsorted(b.cu_seqlens_q, t, side="right") - 1)
+        hv = set(b.heavy[bi].tolist())
+        hv = {s for s in hv if s < vis[j]}
+        assert hv <= set(g[j].tolist()) or len(hv) > K
+
+
+@pytest.mark.parametrize("wi", [1, 2])
+def test_workload_index_scores(wi):
+    b, d = _workload(wi)
+    scores, ld = index_scores(d)
+    sync()
+    rows = _sample_rows(b.T, 3, 10 + wi)
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, rows)
+    check_scores(scores[rows].cpu().numpy().astype(np.float64), sc, vis)
+
+
+def test_workload_mli_two_stream():
+    """Two-layer ragged batch: layer l's attention over its selection runs on
+    the main stream while layer l+1's indexer + top-k run on a second one."""
+    b, d = _workload(4)
+    print(f"workload 4 {b.name}: T={b.T} pages={b.num_pages}", flush=True)
+    sel0, out0, lse0 = decode_step(d, layer=0)
+    aux = torch.cuda.Stream()
+    sel1, out_mli, lse_mli = decode_step(d, layer=1, mode=dsa.DSA_MODE_MLI, attend_idx=sel0,
+                                         mla_layer=0, stream_aux=aux)
+    sync()
+    # attention of the MLI step equals the fused step's (same selection, same layer)
+    assert torch.equal(out_mli, out0) and torch.equal(lse_mli, lse0)
+    rows = _sample_rows(b.T, 6, 44)
+    meta, vis, sc1, s1, f1, K1 = oracle_rows(b, rows, layer=1)
+    check_selection(sel1[rows].cpu().numpy(), s1, f1, K1)
+    g0 = sel0[rows].cpu().numpy()
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], g0, rows, synth.SM_SCALE)
+    check_attention(bf16_to_f64(out_mli[rows]), ref, lse_mli[rows].cpu().numpy(), ref_lse)
+    # adjacent-layer selections overlap heavily (keys differ by 0.1 N(0,1) noise)
+    a, c = sel0.cpu().numpy(), sel1.cpu().numpy()
+    ov = [len(set(a[i][a[i] >= 0]) & set(c[i][c[i] >= 0])) / max(1, (a[i] >= 0).sum())
+          for i in range(b.T)]
+    print(f"selection overlap mean {np.mean(ov):.3f} min {np.min(ov):.3f}", flush=True)
+    assert np.mean(ov) > 0.5
