@@ -11,11 +11,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+# per-file code-generation options: the indexer reads its MFMA results with
+# VALU right away, so they are kept in VGPRs instead of AGPRs
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HEADERS = ["internal.h", "device_common.h"]
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed-fp32 VALU ops in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -34,16 +37,28 @@ def stale() -> bool:
     return any(os.path.getmtime(d) > t for d in deps)
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-x", "hip", *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libdsa.so")
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every source for gfx950 (one object each) and link libdsa.so."""
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="dsa_build_") as tmpdir:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            _run(["hipcc", *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC,
+                  "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

@@ -155,7 +155,7 @@ int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_
   if (!q8 || !q_scale || !w || !k8_cache || !k_scale || !scores)
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   hipError_t e = dsa::launch_index_score(dsa::batch_args(*batch), q8, q_scale, w, k8_cache,
-                                         k_scale, scores, ld, (hipStream_t)stream);
+                                         k_scale, scores, ld, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "index_score launch");
 }
 
@@ -169,6 +169,8 @@ int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t 
   if (batch->num_tokens == 0) return DSA_OK;
   if (!idx || (!scores && batch->max_seqlen_k > 0))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!dsa::topk_supported(dsa::batch_args(*batch), k))
+    return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
   const size_t need = dsa::topk_ws_layout(dsa::batch_args(*batch)).total;
   if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "top-k workspace too small");
   hipError_t e = dsa::launch_topk(dsa::batch_args(*batch), scores, ld, k, idx, ws,
@@ -219,6 +221,8 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (!idx_out || !out || !mla->q || !ix->q8 || !ix->q_scale || !ix->w ||
       (batch->max_seqlen_k > 0 && (!ix->k8_cache || !ix->k_scale || !mla->kv_cache)))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!dsa::topk_supported(dsa::batch_args(*batch), k))
+    return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
   const StepWs L = step_layout(batch, used);
   if (ws_bytes < L.total || !ws) return fail(DSA_ERR_WORKSPACE, "step workspace too small");
   const BatchArgs a = dsa::batch_args(*batch);
@@ -229,12 +233,23 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   const int64_t ld = step_ld(batch);
   hipStream_t sm = (hipStream_t)stream_main;
 
-  if (!mli) {
-    hipError_t e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache,
-                                           ix->k_scale, scores, ld, sm);
+  // indexer + top-k on stream s: the scan also builds the first radix
+  // histogram of each row, so the top-k starts at its threshold step
+  auto select = [&](hipStream_t s) -> int {
+    hipError_t e = dsa::launch_topk_zero(a, topk_ws, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k zero launch");
+    e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
+                                ld, dsa::topk_hist1(a, topk_ws), s);
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
-    e = dsa::launch_topk(a, scores, ld, k, idx_out, topk_ws, sm);
+    e = dsa::launch_topk_select(a, scores, ld, k, idx_out, topk_ws, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return DSA_OK;
+  };
+
+  if (!mli) {
+    rc = select(sm);
+    if (rc) return rc;
+    hipError_t e;
     e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, idx_out, k, mla->sm_scale, out, lse,
                                used, mla_ws, sm);
     if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
@@ -251,11 +266,8 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = hipStreamWaitEvent(sa, ev_start, 0);
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
-                              ld, sa);
-  if (e != hipSuccess) return hip_fail(e, "index_score launch");
-  e = dsa::launch_topk(a, scores, ld, k, idx_out, topk_ws, sa);
-  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  rc = select(sa);
+  if (rc) return rc;
   e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, opts->attend_idx, k, mla->sm_scale, out,
                              lse, used, mla_ws, sm);
   if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");

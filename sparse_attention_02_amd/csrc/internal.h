@@ -49,12 +49,21 @@ int default_splits(const BatchArgs& b, int k);
 // KV splits actually launched for k tokens per row and a requested split count.
 int mla_splits_used(int k, int n_split);
 
+// hist (may be NULL): per-row histogram of the top 11 bits of each score's
+// order-preserving key, [T][kTopkBins], accumulated with atomics.
 hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float* q_scale,
                               const float* w, const uint8_t* k8, const float* k_scale,
-                              float* scores, int64_t ld, hipStream_t s);
+                              float* scores, int64_t ld, uint32_t* hist, hipStream_t s);
 
+// Whole top-k: zero, histogram, threshold, collect, final.
 hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
                        void* ws, hipStream_t s);
+// Pieces used by the fused step, whose indexer builds the histogram.
+hipError_t launch_topk_zero(const BatchArgs& b, void* ws, hipStream_t s);
+hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t ld, int k,
+                              int32_t* idx, void* ws, hipStream_t s);
+uint32_t* topk_hist1(const BatchArgs& b, void* ws);
+bool topk_supported(const BatchArgs& b, int k);
 
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
                              const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,

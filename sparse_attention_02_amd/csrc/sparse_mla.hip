@@ -8,29 +8,39 @@
 // the split / merge structure is stages 2 and 3 of the sparse decode in
 // "Deepseek Details", section DSA).
 //
-// One work-group (8 waves, 512 threads) owns one (row, split) and all 128
+// One work-group (8 waves, two per SIMD) owns one (row, split) and all 128
 // heads, so each gathered latent row is read from HBM once per row.  Wave w
-// owns heads 16w .. 16w+15; its query fragment stays in registers.  Per tile
-// of 32 selected tokens:
-//   gather   positions -> physical slots through the page table; 16-byte
-//            loads of the 1152-byte rows into LDS (row pitch 1168 bytes);
-//   transpose the first 512 dims into a [dim][token] copy in LDS so that the
-//            value product has its contraction (token) dim contiguous;
-//   S^T      = KV Q^T on v_mfma_f32_16x16x32_bf16 (tokens x heads);
-//   softmax  online, per head, in fp32 (max over the tile by two xor steps);
-//   O^T     += V^T P^T on the same MFMA (512 dims x 16 heads per wave), with
-//            P taken straight from the S^T accumulator layout (the token
-//            order of the transposed copy is permuted to match it).
+// owns heads 16w .. 16w+15: its query fragment (16 heads x 576) and its
+// output accumulator (512 dims x 16 heads, fp32) stay in registers
+// (v_mfma_f32_16x16x32_bf16).  Per tile of 32 selected tokens:
+//   gather   slots come from a per-split table built once (position -> page
+//            -> slot); the 1152-byte rows go straight from HBM into LDS with
+//            global_load_lds_dwordx4 (row pitch 1168 bytes), double-buffered:
+//            tile i+1 streams in while tile i computes;
+//   transpose the first 512 dims into a [dim][token] copy so that the value
+//            product has its contraction (token) dim contiguous;
+//   S^T      = KV Q^T (32 tokens x 16 heads per wave);
+//   softmax  online, per head, in fp32; the reference max is only raised
+//            when a score exceeds it by 2^8, so the accumulator is rarely
+//            rescaled (the result does not depend on the reference);
+//   O^T     += V^T P^T (512 dims x 16 heads), P taken straight from the S^T
+//            accumulator layout (the token order of the transposed copy is
+//            permuted to match it).
 #include "device_common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kKsPitch = 1168;  // bytes per token row of the gathered tile
-constexpr int kVtPitch = 80;    // bytes per latent-dim row of the transposed tile
+constexpr int kKsPitch = 1168;                 // bytes per token row of the gathered tile
+constexpr int kKsChunks = kKsPitch / 16;       // 73 (72 data + 1 pad)
+constexpr int kKsLoads = (kMlaTile * kKsChunks + 63) / 64;  // 37 wave-wide 1 KB loads
+constexpr int kKsBytes = kKsLoads * 1024;      // 37888
+constexpr int kVtPitch = 80;                   // bytes per latent-dim row of the transposed tile
+constexpr int kMaxChunk = 2048;                // selected tokens per split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleMargin = 8.f;          // log2 units
 
 union Frag {
   uint4 u;
@@ -43,15 +53,23 @@ __device__ __forceinline__ v8bf lds_frag(const unsigned char* p) {
   return f.v;
 }
 
+// column of token 4q+r in a row of the transposed tile: the order in which the
+// S^T accumulator (16x16 layout: lane group g holds tokens 4g..4g+3 and
+// 16+4g..16+4g+3) hands P to the value product
+__device__ __forceinline__ int quad_pos(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
+
 template <bool SPLIT>
-__global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
-    BatchArgs b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-    const int32_t* __restrict__ idx, int k, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ opart, float* __restrict__ lpart, int n_split,
-    int chunk, int n_work, int per_xcd) {
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[kMlaTile * kKsPitch];
+__global__ __launch_bounds__(kThreads)
+void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                       const int32_t* __restrict__ idx, int k, float scale_log2,
+                       uint16_t* __restrict__ out, float* __restrict__ lse,
+                       float* __restrict__ opart, float* __restrict__ lpart, int n_split, int chunk,
+                       int n_work, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) unsigned char Ks[2][kKsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Vt[DSA_MLA_DV * kVtPitch];
-  __shared__ int64_t rowoff[kMlaTile];
+  __shared__ int32_t slots[kMaxChunk];
+  __shared__ int32_t tile_fb[kMaxChunk / kMlaTile];    // a valid slot of the tile, -1 if none
+  __shared__ uint32_t tile_mask[kMaxChunk / kMlaTile];  // bit x: token x of the tile is valid
 
   // consecutive work items land on the same XCD (work-groups are dealt to
   // the 8 XCDs round-robin), so the splits and the MTP rows of a request
@@ -63,7 +81,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int bi = row_request(b.cu, b.B, t);
   const int v = row_visible(b, bi, t);
   const int j0 = split * chunk;
-  const int j1 = min(k, j0 + chunk);
+  const int ntok = max(0, min(k, j0 + chunk) - j0);
+  const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -71,6 +90,34 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int head = wave * 16 + l16;
+
+  // position -> slot for the whole split (-1: skipped)
+  for (int i = tid; i < ntiles * kMlaTile; i += kThreads) {
+    int slot = -1;
+    if (i < ntok) {
+      const int s = idx[(int64_t)t * k + j0 + i];
+      if (s >= 0 && s < v) {
+        const int64_t sl = slot_of(b, bi, s);
+        if (sl >= 0) slot = (int)sl;
+      }
+    }
+    slots[i] = slot;
+  }
+  __syncthreads();
+  for (int tt = tid; tt < ntiles; tt += kThreads) {
+    int fb = -1;
+    uint32_t mask = 0;
+    for (int x = 0; x < kMlaTile; ++x) {
+      const int sl = slots[tt * kMlaTile + x];
+      if (sl >= 0) {
+        mask |= 1u << x;
+        if (fb < 0) fb = sl;
+      }
+    }
+    tile_fb[tt] = fb;
+    tile_mask[tt] = mask;
+  }
+  __syncthreads();
 
   // B operand of S^T: q[t, head, 32kk + 8g .. +8]
   v8bf qf[18];
@@ -85,123 +132,111 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     }
   }
 
+  // one tile: 37 wave-wide loads of 64 x 16 bytes; lane L of load n fills
+  // byte 16*(64n + L) of the buffer = token (64n+L)/73, chunk (64n+L)%73
+  auto issue_gather = [&](int tile, int buf) {
+    const int fb = tile_fb[tile];
+    if (fb < 0) return;
+    for (int n = wave; n < kKsLoads; n += kThreads / 64) {
+      const int c = 64 * n + lane;
+      const int tok = c / kKsChunks;
+      int cc = c - tok * kKsChunks;
+      int slot = tok < kMlaTile ? slots[tile * kMlaTile + tok] : -1;
+      if (slot < 0) slot = fb;  // padding lanes and skipped tokens re-read a valid row
+      if (cc >= 72) cc = 0;
+      const uint16_t* src = kv + (int64_t)slot * DSA_MLA_DIM + cc * 8;
+      __builtin_amdgcn_global_load_lds(src, Ks[buf] + n * 1024, 16, 0, 0);
+    }
+  };
+
   v4f acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
+  float m_ref = -INFINITY;  // reference max of this lane's head (log2 units)
   float l_run = 0.f;
 
-  for (int j = j0; j < j1; j += kMlaTile) {
-    if (tid < kMlaTile) {
-      int64_t off = -1;
-      if (j + tid < j1) {
-        const int s = idx[(int64_t)t * k + j + tid];
-        if (s >= 0 && s < v) {
-          const int64_t slot = slot_of(b, bi, s);
-          if (slot >= 0) off = slot * DSA_MLA_DIM;
-        }
-      }
-      rowoff[tid] = off;
-    }
-    __syncthreads();
-
-    // gather: 32 tokens x 72 chunks of 16 bytes, in two batches of loads
+  if (ntiles > 0) issue_gather(0, 0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile in Ks[buf]; every wave is done with the previous tile
+    if (tile + 1 < ntiles) issue_gather(tile + 1, buf ^ 1);
+    const bool live = tile_fb[tile] >= 0;
+    if (live) {
+      // transpose dims 0..511: item = (token quad qd, 8-dim chunk dc)
+      const unsigned char* K = Ks[buf];
+      {
+        const int item = tid;
+        const int qd = item & 7;
+        const int dc = item >> 3;
+        const uint4 r0 = *reinterpret_cast<const uint4*>(K + (4 * qd + 0) * kKsPitch + dc * 16);
+        const uint4 r1 = *reinterpret_cast<const uint4*>(K + (4 * qd + 1) * kKsPitch + dc * 16);
+        const uint4 r2 = *reinterpret_cast<const uint4*>(K + (4 * qd + 2) * kKsPitch + dc * 16);
+        const uint4 r3 = *reinterpret_cast<const uint4*>(K + (4 * qd + 3) * kKsPitch + dc * 16);
+        const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+        const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+        const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
+        const uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
+        const int pos = quad_pos(qd);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint4 val[3];
-#pragma unroll
-      for (int r = 0; r < 3; ++r) {
-        const int c = tid + (3 * half + r) * kThreads;
-        val[r] = make_uint4(0u, 0u, 0u, 0u);
-        if (3 * half + r < 5 && c < kMlaTile * 72) {
-          const int tok = c / 72, cc = c - tok * 72;
-          const int64_t off = rowoff[tok];
-          if (off >= 0) val[r] = *reinterpret_cast<const uint4*>(kv + off + cc * 8);
+        for (int e = 0; e < 8; ++e) {
+          const int wi = e >> 1;
+          uint32_t lo, hi;
+          if (e & 1) {
+            lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+            hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+          } else {
+            lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+            hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+          }
+          *reinterpret_cast<uint2*>(Vt + (8 * dc + e) * kVtPitch + pos * 2) = make_uint2(lo, hi);
         }
-      }
-#pragma unroll
-      for (int r = 0; r < 3; ++r) {
-        const int c = tid + (3 * half + r) * kThreads;
-        if (3 * half + r < 5 && c < kMlaTile * 72) {
-          const int tok = c / 72, cc = c - tok * 72;
-          *reinterpret_cast<uint4*>(Ks + tok * kKsPitch + cc * 16) = val[r];
-        }
-      }
-    }
-    __syncthreads();
-
-    // transpose dims 0..511: thread = (token quad qd, 8-dim chunk dc)
-    {
-      const int qd = tid & 7;
-      const int dc = tid >> 3;
-      const uint4 r0 = *reinterpret_cast<const uint4*>(Ks + (4 * qd + 0) * kKsPitch + dc * 16);
-      const uint4 r1 = *reinterpret_cast<const uint4*>(Ks + (4 * qd + 1) * kKsPitch + dc * 16);
-      const uint4 r2 = *reinterpret_cast<const uint4*>(Ks + (4 * qd + 2) * kKsPitch + dc * 16);
-      const uint4 r3 = *reinterpret_cast<const uint4*>(Ks + (4 * qd + 3) * kKsPitch + dc * 16);
-      const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-      const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-      const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
-      const uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
-      // token 4qd + r sits at column 8(qd & 3) + 4(qd >> 2) + r, the order in
-      // which the S^T accumulator hands P to the value product
-      const int pos = 8 * (qd & 3) + 4 * (qd >> 2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-          hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-        } else {
-          lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-          hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-        }
-        *reinterpret_cast<uint2*>(Vt + (8 * dc + e) * kVtPitch + pos * 2) = make_uint2(lo, hi);
       }
     }
     __syncthreads();
+    if (!live) continue;
 
     // S^T (32 tokens x 16 heads) = KV (32 x 576) . Q^T (576 x 16)
+    const unsigned char* K = Ks[buf];
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
-      const v8bf a0 = lds_frag(Ks + l16 * kKsPitch + (4 * kk + g) * 16);
-      const v8bf a1 = lds_frag(Ks + (16 + l16) * kKsPitch + (4 * kk + g) * 16);
+      const v8bf a0 = lds_frag(K + l16 * kKsPitch + (4 * kk + g) * 16);
+      const v8bf a1 = lds_frag(K + (16 + l16) * kKsPitch + (4 * kk + g) * 16);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
     }
     // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
+    const uint32_t mask = tile_mask[tile];
     float z[8];
+    float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[r] = rowoff[4 * g + r] >= 0 ? s0[r] * scale_log2 : -INFINITY;
-      z[4 + r] = rowoff[16 + 4 * g + r] >= 0 ? s1[r] * scale_log2 : -INFINITY;
+      z[r] = (mask >> (4 * g + r)) & 1u ? s0[r] * scale_log2 : -INFINITY;
+      z[4 + r] = (mask >> (16 + 4 * g + r)) & 1u ? s1[r] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, fmaxf(z[r], z[4 + r]));
     }
-    float tmax = z[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, z[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.f;
-    float p[8];
-    if (m_new == -INFINITY) {
+    const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
+    if (__ballot(raise)) {
+      const float m_new = raise ? tmax : m_ref;
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+      if (__ballot(alpha != 1.f && m_ref != -INFINITY)) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) p[r] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) p[r] = exp2f(z[r] - m_new);
+        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      }
+      l_run *= alpha;
+      m_ref = m_new;
     }
+    float p[8];
     float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) psum += p[r];
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+    for (int r = 0; r < 8; ++r) {
+      p[r] = m_ref == -INFINITY ? 0.f : exp2f(z[r] - m_ref);
+      psum += p[r];
     }
+    l_run += psum;
     Frag pf;
     pf.u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7]));
@@ -211,30 +246,29 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       const v8bf a = lds_frag(Vt + (16 * mt + l16) * kVtPitch + 16 * g);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf.v, acc[mt], 0, 0, 0);
     }
-    __syncthreads();
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  const float lse_v = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   // lane holds O^T[16mt + 4g + r][head]
   if (!SPLIT) {
     uint16_t* o = out + ((int64_t)t * DSA_MLA_HEADS + head) * DSA_MLA_DV + 4 * g;
 #pragma unroll
     for (int mt = 0; mt < 32; ++mt) {
-      const v4f a = acc[mt];
+      const v4f x = acc[mt];
       *reinterpret_cast<uint2*>(o + 16 * mt) =
-          make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
+          make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
     }
     if (lse && g == 0) lse[(int64_t)t * DSA_MLA_HEADS + head] = lse_v;
   } else {
     float* o = opart + (((int64_t)t * n_split + split) * DSA_MLA_HEADS + head) * DSA_MLA_DV + 4 * g;
 #pragma unroll
     for (int mt = 0; mt < 32; ++mt) {
-      const v4f a = acc[mt];
-      *reinterpret_cast<float4*>(o + 16 * mt) = make_float4(a[0] * inv, a[1] * inv, a[2] * inv,
-                                                            a[3] * inv);
+      const v4f x = acc[mt];
+      *reinterpret_cast<float4*>(o + 16 * mt) =
+          make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
     }
     if (g == 0) lpart[((int64_t)t * n_split + split) * DSA_MLA_HEADS + head] = lse_v;
   }
@@ -277,6 +311,16 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(const float* __restrict_
   if (lse && threadIdx.x == 0) lse[th] = mx + logf(wsum);
 }
 
+// tokens per split (a multiple of the tile, at most kMaxChunk) and the
+// splits actually used
+void split_shape(int k, int n_split, int* chunk, int* used) {
+  int c = (k + n_split - 1) / n_split;
+  c = (c + kMlaTile - 1) / kMlaTile * kMlaTile;
+  c = std::min(c, kMaxChunk);
+  *chunk = c;
+  *used = (k + c - 1) / c;
+}
+
 }  // namespace
 
 int default_splits(const BatchArgs& b, int k) {
@@ -285,14 +329,6 @@ int default_splits(const BatchArgs& b, int k) {
   int ns = (256 + b.T - 1) / b.T;
   ns = std::min(ns, std::min(max_by_k, kMaxSplits));
   return std::max(ns, 1);
-}
-
-// tokens per split (a multiple of the tile) and the splits actually used
-static void split_shape(int k, int n_split, int* chunk, int* used) {
-  int c = (k + n_split - 1) / n_split;
-  c = (c + kMlaTile - 1) / kMlaTile * kMlaTile;
-  *chunk = c;
-  *used = (k + c - 1) / c;
 }
 
 MlaWs mla_ws_layout(const BatchArgs& b, int n_split) {
@@ -305,6 +341,12 @@ MlaWs mla_ws_layout(const BatchArgs& b, int n_split) {
   off = align_up(off + (size_t)b.T * n_split * DSA_MLA_HEADS * 4, 256);
   w.total = off;
   return w;
+}
+
+int mla_splits_used(int k, int n_split) {
+  int chunk, used;
+  split_shape(k, n_split, &chunk, &used);
+  return used;
 }
 
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
@@ -331,12 +373,6 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
   hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(b.T * DSA_MLA_HEADS)), dim3(128), 0, s,
                      opart, lpart, used, out, lse);
   return hipGetLastError();
-}
-
-int mla_splits_used(int k, int n_split) {
-  int chunk, used;
-  split_shape(k, n_split, &chunk, &used);
-  return used;
 }
 
 }  // namespace dsa

@@ -4,30 +4,37 @@
 // scores; at the k-th score ties go to the lower position ("MTP and sparse
 // attention: NSA and DSA", DSA bullet: each query keeps its top 2048).
 //
-//   1. hist     (row x segment): LDS histogram of the top 11 key bits,
-//               added into a per-row global histogram.
-//   2. thresh   (row): the bin b1 holding the K-th largest key.
-//   3. collect  (row x segment): keys in bins above b1 are selected
-//               outright; keys in b1 are appended to a candidate list.
-//               Appends use one atomic per wave (ballot + mbcnt ranks).
-//   4. final    (row): exact radix select of the remaining count among the
-//               candidates (three 11/11/10-bit passes over the full key),
-//               ties at the threshold resolved by a second radix select on
-//               the position (lowest positions win), then the K positions
-//               are sorted ascending in LDS and written with -1 padding.
-// Output is therefore deterministic: the selected set, ascending.
+//   1. hist1   per-row histogram of the top 11 key bits (LDS histograms added
+//              into global memory).  The fused decode step builds it inside
+//              the indexer scan instead (no extra pass over the scores).
+//   2. thresh  (row): the bin b1 holding the K-th largest key.
+//   3. collect (row x 8192-score segment): keys in bins above b1 are
+//              selected outright, keys in b1 become candidates; one atomic
+//              per work-group reserves the output ranges, ranks inside the
+//              work-group come from a block scan.  It also histograms bits
+//              20..10 of the candidates (hist2).
+//   4. final   (row): the second digit from hist2, the third from one pass
+//              over the candidates, ties at the exact threshold resolved by
+//              a radix select on the position (lowest positions win), then
+//              the K positions are written in ascending order (LDS bitmap,
+//              or a bitonic sort for rows longer than the bitmap).
+// The output is deterministic: the selected set in ascending order.
 #include "device_common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kHistThreads = 256;
+constexpr int kCollectThreads = 256;
+constexpr int kPerThread = kTopkSeg / kCollectThreads;  // 32 scores per thread
 constexpr int kFinalThreads = 1024;
+constexpr int kBitmapWords = 12288;  // 48 KB: rows up to 393216 positions
+constexpr int kSortCap = 4096;       // bitonic fallback (rows longer than the bitmap)
 
 // ctrl words per row
-constexpr int kCtrlB1 = 0;      // threshold bin (-1: every visible position selected)
-constexpr int kCtrlAbove = 1;   // positions written so far as "above"
-constexpr int kCtrlCand = 2;    // candidates appended so far
+constexpr int kCtrlB1 = 0;     // threshold bin (-1: every visible position selected)
+constexpr int kCtrlAbove = 1;  // positions written as "above"
+constexpr int kCtrlCand = 2;   // candidates appended
 constexpr int kCtrlWords = 4;
 
 __global__ void zero_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -95,6 +102,30 @@ __device__ void find_cut(const uint32_t* h, int nbins, uint32_t need, int* bin, 
   __syncthreads();
 }
 
+// Exclusive prefix sum of x over the block (blockDim.x a multiple of 64,
+// at most 1024 threads); *total receives the sum.  `wsum` holds 16 words.
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* wsum,
+                                                        uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t s = wsum[w];
+    if (w < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - x;
+}
+
 __global__ __launch_bounds__(kHistThreads) void topk_thresh_kernel(BatchArgs b, int k,
                                                                     const uint32_t* __restrict__ hist,
                                                                     int32_t* __restrict__ ctrl) {
@@ -114,46 +145,60 @@ __global__ __launch_bounds__(kHistThreads) void topk_thresh_kernel(BatchArgs b, 
   if (threadIdx.x == 0) ctrl[t * kCtrlWords + kCtrlB1] = s_bin;
 }
 
-// Appends the lanes whose pred is set to list at ranks taken from one
-// atomic counter per wave; returns nothing.  Order among lanes follows the
-// lane index; order among waves follows the atomics.
-template <typename T>
-__device__ __forceinline__ void wave_append(bool pred, T value, T* list, int32_t* counter) {
-  const uint64_t mask = __ballot(pred);
-  if (mask == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((long long)mask) - 1;
-  int base = 0;
-  if (lane == leader) base = atomicAdd(counter, __popcll(mask));
-  base = __shfl(base, leader);
-  if (pred) {
-    const uint64_t below = lane ? (mask & ((~0ull) >> (64 - lane))) : 0ull;
-    list[base + __popcll(below)] = value;
-  }
-}
-
-__global__ __launch_bounds__(kHistThreads) void topk_collect_kernel(
+__global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
     BatchArgs b, const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ ctrl,
-    int32_t* __restrict__ idx, uint2* __restrict__ cand, int64_t cand_stride) {
+    int32_t* __restrict__ idx, uint2* __restrict__ cand, int64_t cand_stride,
+    uint32_t* __restrict__ hist2) {
+  __shared__ uint32_t h2[kTopkBins];
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t s_base[2];
   const int t = blockIdx.x;
   const int v = row_len(b, t);
   const int s0 = blockIdx.y * kTopkSeg;
   if (s0 >= v) return;
-  const int s1 = min(v, s0 + kTopkSeg);
   const int b1 = ctrl[t * kCtrlWords + kCtrlB1];
   const float* row = scores + (int64_t)t * ld;
-  int32_t* out = idx + (int64_t)t * k;
-  uint2* cl = cand + (int64_t)t * cand_stride;
-  // every lane of a wave runs the same number of iterations (ballots)
-  for (int base = s0; base < s1; base += kHistThreads) {
-    const int s = base + threadIdx.x;
-    const bool in = s < s1;
-    const uint32_t key = in ? float_key(row[s]) : 0u;
-    const int d = (int)(key >> 21);
-    const bool above = in && (b1 < 0 || d > b1);
-    const bool eq = in && b1 >= 0 && d == b1;
-    wave_append<int32_t>(above, s, out, &ctrl[t * kCtrlWords + kCtrlAbove]);
-    wave_append<uint2>(eq, make_uint2(key, (uint32_t)s), cl, &ctrl[t * kCtrlWords + kCtrlCand]);
+  for (int i = threadIdx.x; i < kTopkBins; i += kCollectThreads) h2[i] = 0u;
+
+  // element j of this thread is position s0 + tid + 256 j (coalesced loads)
+  uint32_t key[kPerThread];
+  uint32_t am = 0, em = 0;  // bit j: element j is above / a candidate
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int s = s0 + threadIdx.x + j * kCollectThreads;
+    key[j] = s < v ? float_key(row[s]) : 0u;
+    const int d = (int)(key[j] >> 21);
+    if (s < v) {
+      if (b1 < 0 || d > b1) am |= 1u << j;
+      else if (d == b1) em |= 1u << j;
+    }
+  }
+  __syncthreads();  // h2 zeroed
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (em & (1u << j)) atomicAdd(&h2[(key[j] >> 10) & (kTopkBins - 1)], 1u);
+
+  uint32_t tot_a, tot_e;
+  const uint32_t ex_a = block_exclusive_sum(__popc(am), wsum, &tot_a);
+  const uint32_t ex_e = block_exclusive_sum(__popc(em), wsum, &tot_e);
+  if (threadIdx.x == 0) {
+    s_base[0] = tot_a ? atomicAdd(&ctrl[t * kCtrlWords + kCtrlAbove], (int)tot_a) : 0;
+    s_base[1] = tot_e ? atomicAdd(&ctrl[t * kCtrlWords + kCtrlCand], (int)tot_e) : 0;
+  }
+  __syncthreads();
+  int32_t* out = idx + (int64_t)t * k + s_base[0] + ex_a;
+  uint2* cl = cand + (int64_t)t * cand_stride + s_base[1] + ex_e;
+  int na = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int s = s0 + threadIdx.x + j * kCollectThreads;
+    if (am & (1u << j)) out[na++] = s;
+    if (em & (1u << j)) cl[ne++] = make_uint2(key[j], (uint32_t)s);
+  }
+  if (b1 >= 0) {
+    uint32_t* gh = hist2 + (int64_t)t * kTopkBins;
+    for (int i = threadIdx.x; i < kTopkBins; i += kCollectThreads)
+      if (h2[i]) atomicAdd(&gh[i], h2[i]);
   }
 }
 
@@ -190,63 +235,119 @@ __device__ uint32_t radix_select(int n, uint32_t need, Get get, uint32_t* h, uin
   return prefix;
 }
 
-__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(BatchArgs b, int k,
-                                                                  const int32_t* __restrict__ ctrl,
-                                                                  int32_t* __restrict__ idx,
-                                                                  const uint2* __restrict__ cand,
-                                                                  int64_t cand_stride) {
-  __shared__ int32_t sel[DSA_MAX_TOPK];
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
+    BatchArgs b, int k, const int32_t* __restrict__ ctrl, const uint32_t* __restrict__ hist2,
+    int32_t* __restrict__ idx, const uint2* __restrict__ cand, int64_t cand_stride) {
+  __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ int32_t sel[kSortCap];
   __shared__ uint32_t h[kTopkBins];
   __shared__ uint32_t scan[kFinalThreads];
+  __shared__ uint32_t wsum[16];
   __shared__ int s_bin;
   __shared__ uint32_t s_above;
   __shared__ int32_t s_count;
   const int t = blockIdx.x;
   const int v = row_len(b, t);
   const int K = min(k, v);
-  const int n_above = ctrl[t * kCtrlWords + kCtrlAbove];
+  const int n_above = min(ctrl[t * kCtrlWords + kCtrlAbove], K);
   const int nc = ctrl[t * kCtrlWords + kCtrlCand];
+  const int b1 = ctrl[t * kCtrlWords + kCtrlB1];
   int32_t* out = idx + (int64_t)t * k;
   const uint2* cl = cand + (int64_t)t * cand_stride;
-
-  for (int i = threadIdx.x; i < n_above && i < K; i += kFinalThreads) sel[i] = out[i];
-  if (threadIdx.x == 0) s_count = min(n_above, K);
-  __syncthreads();
-
   const int need = K - n_above;
-  if (need > 0 && nc > 0) {
-    uint32_t gt = 0;
-    const uint32_t tau = radix_select(
-        nc, (uint32_t)need,
-        [&](int i, uint32_t* x) {
-          *x = cl[i].x;
-          return true;
-        },
-        h, scan, &s_bin, &s_above, &gt);
-    const uint32_t need_eq = (uint32_t)need - gt;
-    // among keys equal to tau keep the need_eq lowest positions:
-    // radix-select the need_eq largest of ~pos
-    uint32_t gt2 = 0;
-    const uint32_t npos = radix_select(
-        nc, need_eq,
-        [&](int i, uint32_t* x) {
-          const uint2 c = cl[i];
-          *x = ~c.y;
-          return c.x == tau;
-        },
-        h, scan, &s_bin, &s_above, &gt2);
-    const uint32_t pcut = ~npos;  // positions <= pcut among ties are kept
+
+  uint32_t tau = 0xffffffffu, pcut = 0u;  // nothing from the candidates by default
+  if (need > 0 && nc > 0 && b1 >= 0) {
+    // second digit (key bits 20..10) from the collect pass's histogram
+    for (int i = threadIdx.x; i < kTopkBins; i += kFinalThreads)
+      h[i] = hist2[(int64_t)t * kTopkBins + i];
+    __syncthreads();
+    find_cut(h, kTopkBins, (uint32_t)need, &s_bin, &s_above, scan);
+    const int b2 = s_bin;
+    const uint32_t need2 = (uint32_t)need - s_above;
+    // third digit (bits 9..0) over the candidates in (b1, b2)
+    for (int i = threadIdx.x; i < 1024; i += kFinalThreads) h[i] = 0u;
+    __syncthreads();
     for (int i = threadIdx.x; i < nc; i += kFinalThreads) {
-      const uint2 c = cl[i];
-      if (c.x > tau || (c.x == tau && c.y <= pcut)) {
-        const int at = atomicAdd(&s_count, 1);
-        if (at < DSA_MAX_TOPK) sel[at] = (int32_t)c.y;
+      const uint32_t x = cl[i].x;
+      if (((x >> 10) & (kTopkBins - 1)) == (uint32_t)b2) atomicAdd(&h[x & 1023u], 1u);
+    }
+    __syncthreads();
+    find_cut(h, 1024, need2, &s_bin, &s_above, scan);
+    const int b3 = s_bin;
+    const uint32_t need3 = need2 - s_above;
+    const uint32_t cnt_eq = h[b3];
+    tau = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10) | (uint32_t)b3;
+    pcut = 0xffffffffu;
+    __syncthreads();
+    if (need3 < cnt_eq) {
+      // keep the need3 lowest positions among keys equal to tau: the need3
+      // largest values of ~position
+      uint32_t gt2 = 0;
+      const uint32_t t_ = tau;
+      const uint32_t npos = radix_select(
+          nc, need3,
+          [&](int i, uint32_t* x) {
+            const uint2 c = cl[i];
+            *x = ~c.y;
+            return c.x == t_;
+          },
+          h, scan, &s_bin, &s_above, &gt2);
+      pcut = ~npos;
+    }
+  }
+  auto picked = [&](uint2 c) { return c.x > tau || (c.x == tau && c.y <= pcut); };
+
+  if (v <= kBitmapWords * 32) {
+    const int nwords = (v + 31) >> 5;
+    for (int i = threadIdx.x; i < nwords; i += kFinalThreads) bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_above; i += kFinalThreads) {
+      const int s = out[i];
+      atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+    }
+    if (tau != 0xffffffffu || pcut != 0u) {
+      for (int i = threadIdx.x; i < nc; i += kFinalThreads) {
+        const uint2 c = cl[i];
+        if (picked(c)) atomicOr(&bitmap[c.y >> 5], 1u << (c.y & 31));
       }
     }
     __syncthreads();
+    // ascending compaction: thread i owns words [i*per, (i+1)*per)
+    const int per = (nwords + kFinalThreads - 1) / kFinalThreads;
+    const int w0 = threadIdx.x * per, w1 = min(nwords, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
+    uint32_t total;
+    uint32_t at = block_exclusive_sum(cnt, wsum, &total);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t m = bitmap[w];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        if (at < (uint32_t)K) out[at] = (w << 5) + bit;
+        ++at;
+      }
+    }
+    __syncthreads();
+    for (int i = (int)min(total, (uint32_t)K) + threadIdx.x; i < k; i += kFinalThreads) out[i] = -1;
+    return;
   }
 
-  // bitonic sort of sel[0..K) ascending (padding with INT_MAX)
+  // long rows: gather into LDS and sort (K <= kSortCap)
+  for (int i = threadIdx.x; i < n_above; i += kFinalThreads) sel[i] = out[i];
+  if (threadIdx.x == 0) s_count = n_above;
+  __syncthreads();
+  if (tau != 0xffffffffu || pcut != 0u) {
+    for (int i = threadIdx.x; i < nc; i += kFinalThreads) {
+      const uint2 c = cl[i];
+      if (picked(c)) {
+        const int a = atomicAdd(&s_count, 1);
+        if (a < kSortCap) sel[a] = (int32_t)c.y;
+      }
+    }
+  }
+  __syncthreads();
   int n2 = 1;
   while (n2 < K) n2 <<= 1;
   for (int i = K + threadIdx.x; i < n2; i += kFinalThreads) sel[i] = 0x7fffffff;
@@ -274,8 +375,8 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(BatchArgs b, 
 TopkWs topk_ws_layout(const BatchArgs& b) {
   TopkWs w;
   size_t off = 0;
-  w.hist_off = off;
-  off = align_up(off + (size_t)b.T * kTopkBins * 4, 256);
+  w.hist_off = off;  // hist1 then hist2, [T][2048] each
+  off = align_up(off + (size_t)b.T * kTopkBins * 4 * 2, 256);
   w.ctrl_off = off;
   off = align_up(off + (size_t)b.T * kCtrlWords * 4, 256);
   w.cand_off = off;
@@ -284,28 +385,56 @@ TopkWs topk_ws_layout(const BatchArgs& b) {
   return w;
 }
 
-hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, hipStream_t s) {
+bool topk_supported(const BatchArgs& b, int k) {
+  // rows longer than the bitmap are sorted in LDS, which holds kSortCap
+  return (int64_t)b.max_seqlen_k <= (int64_t)kBitmapWords * 32 || k <= kSortCap;
+}
+
+uint32_t* topk_hist1(const BatchArgs& b, void* ws) {
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + topk_ws_layout(b).hist_off);
+}
+
+hipError_t launch_topk_zero(const BatchArgs& b, void* ws, hipStream_t s) {
+  if (b.T == 0) return hipSuccess;
+  const TopkWs L = topk_ws_layout(b);
+  // histograms and control words start at zero (a fill kernel, not a
+  // memset, so the sequence can be captured in a graph)
+  const int64_t nz = (int64_t)(L.cand_off / 4);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)),
+                     dim3(256), 0, s, static_cast<uint32_t*>(ws), nz);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t ld, int k,
+                              int32_t* idx, void* ws, hipStream_t s) {
   if (b.T == 0) return hipSuccess;
   const TopkWs L = topk_ws_layout(b);
   char* base = static_cast<char*>(ws);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist_off);
+  uint32_t* hist1 = reinterpret_cast<uint32_t*>(base + L.hist_off);
+  uint32_t* hist2 = hist1 + (size_t)b.T * kTopkBins;
   int32_t* ctrl = reinterpret_cast<int32_t*>(base + L.ctrl_off);
   uint2* cand = reinterpret_cast<uint2*>(base + L.cand_off);
-  // histogram and control words start at zero (a fill kernel, not a memset,
-  // so the sequence can be captured in a graph)
-  const int64_t nz = (int64_t)(L.cand_off / 4);
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)),
-                     dim3(256), 0, s, reinterpret_cast<uint32_t*>(base), nz);
   const int segs = std::max(1, (b.max_seqlen_k + kTopkSeg - 1) / kTopkSeg);
   dim3 g2(b.T, segs);
-  hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(kHistThreads), 0, s, b, scores, ld, k, hist);
-  hipLaunchKernelGGL(topk_thresh_kernel, dim3(b.T), dim3(kHistThreads), 0, s, b, k, hist, ctrl);
-  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kHistThreads), 0, s, b, scores, ld, k, ctrl,
+  hipLaunchKernelGGL(topk_thresh_kernel, dim3(b.T), dim3(kHistThreads), 0, s, b, k, hist1, ctrl);
+  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k, ctrl,
+                     idx, cand, (int64_t)b.max_seqlen_k, hist2);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(b.T), dim3(kFinalThreads), 0, s, b, k, ctrl, hist2,
                      idx, cand, (int64_t)b.max_seqlen_k);
-  hipLaunchKernelGGL(topk_final_kernel, dim3(b.T), dim3(kFinalThreads), 0, s, b, k, ctrl, idx,
-                     cand, (int64_t)b.max_seqlen_k);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
+                       void* ws, hipStream_t s) {
+  if (b.T == 0) return hipSuccess;
+  hipError_t e = launch_topk_zero(b, ws, s);
+  if (e != hipSuccess) return e;
+  const int segs = std::max(1, (b.max_seqlen_k + kTopkSeg - 1) / kTopkSeg);
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(b.T, segs), dim3(kHistThreads), 0, s, b, scores, ld, k,
+                     topk_hist1(b, ws));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_select(b, scores, ld, k, idx, ws, s);
 }
 
 }  // namespace dsa

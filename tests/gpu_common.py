@@ -17,8 +17,11 @@ K = synth.TOPK
 # row's largest score is a real defect (a wrong head, scale or position).
 SCORE_RTOL = 2e-5
 # Attention outputs (bf16): the contract's absolute bounds, also applied
-# relative to the reference's rms per (row, head) because the default
-# workload's outputs are ~1e-3 in size.
+# relative to the reference's rms per (row, head) for the default value
+# scale, whose outputs are ~1e-3 in size.  (With N(0,1) q and kv the bf16
+# rounding of the softmax weights alone gives errors ~2^-9 of |kv|, a few
+# percent of the output rms after averaging, so there the absolute bounds
+# are the bar.)
 OUT_MAX_ABS, OUT_MEAN_ABS = 2e-2, 2e-3
 # lse in fp32 from exact bf16 products summed in fp32: 1e-3 absolute.
 LSE_ATOL = 1e-3

@@ -132,7 +132,7 @@ def test_sparse_mla_small_oracle_selection(ci, n_split, stress):
     out, lse = sparse_mla(d, idx, n_split=n_split)
     sync()
     ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], sel, list(range(b.T)), synth.SM_SCALE)
-    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse)
+    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse, relative=not stress)
 
 
 def test_sparse_mla_split_invariance_and_determinism():
@@ -145,10 +145,12 @@ def test_sparse_mla_split_invariance_and_determinism():
     o4b, l4b = sparse_mla(d, idx, n_split=4)
     sync()
     assert torch.equal(o4, o4b) and torch.equal(l4, l4b)
-    # the split count changes only fp32 rounding before the final bf16
-    # rounding: at most one bf16 ulp apart (2^-7 relative covers 1-2 ulps)
+    # besides the final bf16 rounding (one ulp, 2^-8 relative) the split
+    # changes the running max that P is taken against, so P's bf16 rounding
+    # differs by up to 2^-9 of each weight: at most ~2^-9 * max|kv| absolute
     a, c = o1.float(), o4.float()
-    assert ((a - c).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), c.abs()) + 1e-6).all()
+    kvmax = float(np.abs(bf16_to_f64(d.kv[0])).max())
+    assert ((a - c).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), c.abs()) + 2.0 ** -9 * kvmax).all()
     assert (l1 - l4).abs().max().item() <= 1e-4
 
 
@@ -167,7 +169,7 @@ def test_sparse_mla_handles_unsorted_padded_and_invalid_positions():
     sync()
     meta = O.Meta.of(b)
     ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], sel, [0, 1], synth.SM_SCALE)
-    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse)
+    check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse, relative=False)
 
 
 def test_page_permutation_invariance_bitwise():
@@ -191,7 +193,7 @@ def test_page_permutation_invariance_bitwise():
 
 @pytest.mark.parametrize("ci", range(len(SMALL)))
 def test_decode_step_small(ci):
-    b = _small(SMALL[ci], 900 + ci, mla_scale=1.0)
+    b = _small(SMALL[ci], 900 + ci)
     d = to_device(b)
     idx, out, lse = decode_step(d)
     idx2, out2, lse2 = decode_step(d)
@@ -236,12 +238,10 @@ def test_workload_decode_step(wi):
     g = idx[rows].cpu().numpy()
     check_selection(g, sel, flags, Ks)
     ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], g, rows, synth.SM_SCALE)
-    # the oracle over the GPU's selection, per row
-    gi = np.zeros((len(rows), K), np.int32)
-    gi[:] = g
     check_attention(bf16_to_f64(out[rows]), ref, lse[rows].cpu().numpy(), ref_lse)
-    # heavy tokens are always selected
-    for j, t in enumerate(rows):
+    # decode rows always select the heavy tokens (prefill rows need not: the
+    # heavy direction follows the sum over all 4096 rows)
+    for j, t in enumerate(rows if b.max_q <= 2 else []):
         bi = int(np.searchsorted(b.cu_seqlens_q, t, side="right") - 1)
         hv = set(b.heavy[bi].tolist())
         hv = {s for s in hv if s < vis[j]}
