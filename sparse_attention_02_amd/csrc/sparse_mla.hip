@@ -32,11 +32,15 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kKsPitch = 1168;                 // bytes per token row of the gathered tile
-constexpr int kKsChunks = kKsPitch / 16;       // 73 (72 data + 1 pad)
+// Row pitches are chosen for gfx950's LDS (64 banks of 4 bytes): a
+// ds_read_b128 whose lanes l%16 pick rows and l/16 pick 16-byte columns is
+// conflict-free when the pitch is 32 mod 64 bytes (measured: 1152 or 1168
+// bytes cost 1.65-3x more).
+constexpr int kKsPitch = 1184;                 // bytes per token row of the gathered tile
+constexpr int kKsChunks = kKsPitch / 16;       // 74 (72 data + 2 pad)
 constexpr int kKsLoads = (kMlaTile * kKsChunks + 63) / 64;  // 37 wave-wide 1 KB loads
 constexpr int kKsBytes = kKsLoads * 1024;      // 37888
-constexpr int kVtPitch = 80;                   // bytes per latent-dim row of the transposed tile
+constexpr int kVtPitch = 96;                   // bytes per latent-dim row of the transposed tile
 constexpr int kMaxChunk = 2048;                // selected tokens per split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -143,7 +147,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
       int cc = c - tok * kKsChunks;
       int slot = tok < kMlaTile ? slots[tile * kMlaTile + tok] : -1;
       if (slot < 0) slot = fb;  // padding lanes and skipped tokens re-read a valid row
-      if (cc >= 72) cc = 0;
+      if (cc >= 72) cc = 0;  // pad chunks
       const uint16_t* src = kv + (int64_t)slot * DSA_MLA_DIM + cc * 8;
       __builtin_amdgcn_global_load_lds(src, Ks[buf] + n * 1024, 16, 0, 0);
     }
@@ -163,12 +167,16 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     if (tile + 1 < ntiles) issue_gather(tile + 1, buf ^ 1);
     const bool live = tile_fb[tile] >= 0;
     if (live) {
-      // transpose dims 0..511: item = (token quad qd, 8-dim chunk dc)
+      // transpose dims 0..511: lane (qd = lane/8, dc = 8*wave + lane%8) reads
+      // 4 token rows of one 16-byte column (lanes 0-7 read 128 contiguous
+      // bytes of a row, lanes 8-15 the row 4 below: disjoint banks) and
+      // writes its 8 dims in a lane-rotated order so that the 8 rows written
+      // together by lanes 0-7 fall in different banks
       const unsigned char* K = Ks[buf];
       {
-        const int item = tid;
-        const int qd = item & 7;
-        const int dc = item >> 3;
+        const int rot = lane & 7;
+        const int qd = lane >> 3;
+        const int dc = 8 * wave + rot;
         const uint4 r0 = *reinterpret_cast<const uint4*>(K + (4 * qd + 0) * kKsPitch + dc * 16);
         const uint4 r1 = *reinterpret_cast<const uint4*>(K + (4 * qd + 1) * kKsPitch + dc * 16);
         const uint4 r2 = *reinterpret_cast<const uint4*>(K + (4 * qd + 2) * kKsPitch + dc * 16);
@@ -178,16 +186,26 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
         const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
         const uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
         const int pos = quad_pos(qd);
+        // dims (2wi, 2wi+1) of the 4 tokens: low and high halves of word wi
+        uint32_t lo_e[4], hi_e[4], lo_o[4], hi_o[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int wi = 0; wi < 4; ++wi) {
+          lo_e[wi] = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+          hi_e[wi] = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+          lo_o[wi] = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+          hi_o[wi] = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int step = 0; step < 8; ++step) {
+          const int e = (step + rot) & 7;  // this lane's dim at this step
           const int wi = e >> 1;
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-            hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-          } else {
-            lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-            hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+          uint32_t lo = lo_e[0], hi = hi_e[0];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (wi == c) {
+              lo = (e & 1) ? lo_o[c] : lo_e[c];
+              hi = (e & 1) ? hi_o[c] : hi_e[c];
+            }
           }
           *reinterpret_cast<uint2*>(Vt + (8 * dc + e) * kVtPitch + pos * 2) = make_uint2(lo, hi);
         }

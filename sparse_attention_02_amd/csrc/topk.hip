@@ -62,8 +62,16 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(BatchArgs b,
   for (int i = threadIdx.x; i < kTopkBins; i += kHistThreads) h[i] = 0u;
   __syncthreads();
   const float* row = scores + (int64_t)t * ld;
-  for (int s = s0 + threadIdx.x; s < s1; s += kHistThreads)
-    atomicAdd(&h[float_key(row[s]) >> 21], 1u);
+  // batches of 8 independent loads per thread
+  for (int base = s0; base < s1; base += 8 * kHistThreads) {
+    uint32_t kk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      kk[u] = float_key(row[min(base + (int)threadIdx.x + u * kHistThreads, s1 - 1)]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (base + (int)threadIdx.x + u * kHistThreads < s1) atomicAdd(&h[kk[u] >> 21], 1u);
+  }
   __syncthreads();
   uint32_t* gh = hist + (int64_t)t * kTopkBins;
   for (int i = threadIdx.x; i < kTopkBins; i += kHistThreads)
@@ -160,13 +168,17 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   const float* row = scores + (int64_t)t * ld;
   for (int i = threadIdx.x; i < kTopkBins; i += kCollectThreads) h2[i] = 0u;
 
-  // element j of this thread is position s0 + tid + 256 j (coalesced loads)
+  // element j of this thread is position s0 + tid + 256 j (coalesced
+  // loads, all issued before any is used: positions past the row re-read
+  // its last score and are masked below)
   uint32_t key[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    key[j] = float_key(row[min(s0 + (int)threadIdx.x + j * kCollectThreads, v - 1)]);
   uint32_t am = 0, em = 0;  // bit j: element j is above / a candidate
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int s = s0 + threadIdx.x + j * kCollectThreads;
-    key[j] = s < v ? float_key(row[s]) : 0u;
     const int d = (int)(key[j] >> 21);
     if (s < v) {
       if (b1 < 0 || d > b1) am |= 1u << j;
@@ -202,6 +214,20 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   }
 }
 
+// Calls f(c) for every candidate c in cl[0..n), with each thread's loads
+// issued in batches of 8 before any is used.
+template <typename F>
+__device__ __forceinline__ void for_each_cand(const uint2* __restrict__ cl, int n, F f) {
+  for (int base = 0; base < n; base += 8 * (int)blockDim.x) {
+    uint2 c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = cl[min(base + (int)threadIdx.x + u * (int)blockDim.x, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (base + (int)threadIdx.x + u * (int)blockDim.x < n) f(c[u]);
+  }
+}
+
 // Threshold x* of the `need` largest values among the items accepted by
 // `get` (3 radix passes of 11, 11, 10 bits): count(x > x*) < need <=
 // count(x >= x*).  Returns x*; *gt receives count(x > x*).
@@ -219,11 +245,17 @@ __device__ uint32_t radix_select(int n, uint32_t need, Get get, uint32_t* h, uin
     const int hs = sh + widths[pass];  // bits above this digit must match prefix
     for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      uint32_t x;
-      if (!get(i, &x)) continue;
-      if (hs < 32 && (x >> hs) != (prefix >> hs)) continue;
-      atomicAdd(&h[(x >> sh) & (nb - 1)], 1u);
+    for (int base = 0; base < n; base += 4 * (int)blockDim.x) {
+      uint32_t xs[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ok[u] = get(min(base + (int)threadIdx.x + u * (int)blockDim.x, n - 1), &xs[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (base + (int)threadIdx.x + u * (int)blockDim.x >= n || !ok[u]) continue;
+        if (hs < 32 && (xs[u] >> hs) != (prefix >> hs)) continue;
+        atomicAdd(&h[(xs[u] >> sh) & (nb - 1)], 1u);
+      }
     }
     __syncthreads();
     find_cut(h, nb, need - done_above, s_bin, s_above, scan);
@@ -268,10 +300,9 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     // third digit (bits 9..0) over the candidates in (b1, b2)
     for (int i = threadIdx.x; i < 1024; i += kFinalThreads) h[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < nc; i += kFinalThreads) {
-      const uint32_t x = cl[i].x;
-      if (((x >> 10) & (kTopkBins - 1)) == (uint32_t)b2) atomicAdd(&h[x & 1023u], 1u);
-    }
+    for_each_cand(cl, nc, [&](uint2 c) {
+      if (((c.x >> 10) & (kTopkBins - 1)) == (uint32_t)b2) atomicAdd(&h[c.x & 1023u], 1u);
+    });
     __syncthreads();
     find_cut(h, 1024, need2, &s_bin, &s_above, scan);
     const int b3 = s_bin;
@@ -307,10 +338,9 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
       atomicOr(&bitmap[s >> 5], 1u << (s & 31));
     }
     if (tau != 0xffffffffu || pcut != 0u) {
-      for (int i = threadIdx.x; i < nc; i += kFinalThreads) {
-        const uint2 c = cl[i];
+      for_each_cand(cl, nc, [&](uint2 c) {
         if (picked(c)) atomicOr(&bitmap[c.y >> 5], 1u << (c.y & 31));
-      }
+      });
     }
     __syncthreads();
     // ascending compaction: thread i owns words [i*per, (i+1)*per)
@@ -339,13 +369,12 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   if (threadIdx.x == 0) s_count = n_above;
   __syncthreads();
   if (tau != 0xffffffffu || pcut != 0u) {
-    for (int i = threadIdx.x; i < nc; i += kFinalThreads) {
-      const uint2 c = cl[i];
+    for_each_cand(cl, nc, [&](uint2 c) {
       if (picked(c)) {
         const int a = atomicAdd(&s_count, 1);
         if (a < kSortCap) sel[a] = (int32_t)c.y;
       }
-    }
+    });
   }
   __syncthreads();
   int n2 = 1;
