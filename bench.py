@@ -5,7 +5,19 @@ absorbed-MLA split-KV decode + LSE merge) over the decode batch of 64
 requests x 2 query rows (1 + MTP) at a 131072-token context, on seeded
 synthetic inputs resident in HBM.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Inside the timed steps the library records HIP events around each stage
+on the stream the stage runs on; the roofline of the dominant kernel (the
+indexer scan) is its algorithmic bytes over the average of those per-launch
+durations.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extras]
+  python bench.py --summarize-trace DIR            (rocprofv3 --kernel-trace --stats output)
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR   (two rocprofv3 --pmc runs)
+
+--extras adds two more measurements to the line: the prefill-chunk form
+(4096 query rows on a 61440-token prefix: indexer FP8 MFMA utilisation) and
+the two-stream multi-layer-indexer step on a ragged 48-request batch
+(selection overlap of adjacent layers, time against the one-stream step).
 """
 from __future__ import annotations
 
@@ -20,26 +32,186 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode query-tokens/s at 128K ctx (indexer+top-2048+sparse MLA), % HBM peak"
 HBM_PEAK_GBS = 8000.0
-WORKLOAD = 2
+FP8_PEAK_TFLOPS = 5000.0
+DECODE_WORKLOAD = 2
+PREFILL_WORKLOAD = 3
+MLI_WORKLOAD = 4
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTERS_SUMMARY = os.path.join(PROFILES, "counters.index_score_kernel.decode-b64-mtp1-ctx131072.md")
+# the sources that make up the indexer scan kernel: its counters describe it
+# only while these are unchanged
+INDEXER_SOURCES = ["sparse_attention_02_amd/csrc/indexer.hip",
+                   "sparse_attention_02_amd/csrc/device_common.h",
+                   "sparse_attention_02_amd/csrc/internal.h",
+                   "sparse_attention_02_amd/build.py"]
+# FETCH_SIZE reads half the bytes a plain copy kernel of known size moves,
+# WRITE_SIZE all of them (the device copy of 2 GiB in this script: FETCH_SIZE
+# 1048588 KiB, WRITE_SIZE 2097152 KiB), so the counters are scaled by these
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_stream(fn, iters, warmup=2):
-    """Average ms of fn() over iters, by HIP events on the current stream."""
+def indexer_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in INDEXER_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the indexer scan from the committed counter
+    summary, or None if there is none or the kernel changed since."""
+    try:
+        text = open(COUNTERS_SUMMARY).read()
+    except OSError:
+        return None
+    vals = dict(line.split(":", 1) for line in text.splitlines()
+                if line.startswith(("source_hash:", "hbm_bytes_per_launch:")))
+    if vals.get("source_hash", "").strip() != indexer_source_hash():
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def _short(name):
+    name = name.replace("dsa::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(dsa::")[0].split("(float")[0].split("(unsigned")[0][:60]
+
+
+def summarize_trace(d):
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    print("| kernel | calls | avg us | min us | max us | % time |\n|---|---|---|---|---|---|")
+    for r in csv.DictReader(open(f)):
+        print(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+              f"{float(r['Percentage']):.2f} |")
+
+
+def summarize_counters(fetch_dir, write_dir):
+    import collections
+    import csv
+    import glob
+    vals = {}
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == c:
+                agg[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        vals[c] = {k: (len(v), sum(v) / len(v)) for k, v in agg.items()}
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |\n"
+          "|---|---|---|---|---|")
+    idx = None
+    for k, (n, fk) in vals["FETCH_SIZE"].items():
+        wk = vals["WRITE_SIZE"].get(k, (0, 0.0))[1]
+        hbm = 1024 * (FETCH_SCALE * fk + WRITE_SCALE * wk)
+        print(f"| {k} | {n} | {fk:.0f} | {wk:.0f} | {hbm:.4g} |")
+        if k.startswith("index_score_kernel"):
+            idx = hbm
+    print(f"\nfetch_scale: {FETCH_SCALE}\nwrite_scale: {WRITE_SCALE}")
+    if idx is not None:
+        print(f"hbm_bytes_per_launch: {idx:.0f}\nsource_hash: {indexer_source_hash()}")
+
+
+class Step:
+    """Buffers and the call of one dsa_decode_step over a batch on the GPU."""
+
+    def __init__(self, b, d, mode=0, attend_idx=None, layer=0, mla_layer=None):
+        import torch
+
+        import sparse_attention_02_amd as dsa
+        import synth
+        self.dsa, self.torch = dsa, torch
+        self.d, self.T, self.k = d, b.T, synth.TOPK
+        mla_layer = layer if mla_layer is None else mla_layer
+        self.mode, self.attend_idx = mode, attend_idx
+        self.ws_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_DECODE_STEP, d.meta, self.k, 0)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.idx = torch.empty((b.T, self.k), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((b.T, 128, 512), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((b.T, 128), dtype=torch.float32, device="cuda")
+        self.ix = dict(q8=d.q8, q_scale=d.q_scale, w=d.w, k8_cache=d.k8[layer],
+                       k_scale=d.k_scale[layer])
+        self.ml = dict(q=d.q[mla_layer], kv_cache=d.kv[mla_layer], sm_scale=synth.SM_SCALE)
+        self.aux = torch.cuda.Stream() if mode == dsa.DSA_MODE_MLI else None
+
+    def __call__(self, events=None):
+        self.dsa.dsa_decode_step(self.d.meta, self.ix, self.ml, self.k, self.mode, 0,
+                                 self.attend_idx, self.idx, self.out, self.lse, self.ws,
+                                 self.ws_bytes, stream_aux=self.aux, stage_events=events)
+
+
+def stage_event_sets(n):
+    """n sets of 2 * DSA_NUM_STAGES timing events, each created by one record."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    sets = []
+    for _ in range(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * dsa.DSA_NUM_STAGES)]
+        for e in evs:
+            e.record()
+        sets.append(evs)
+    torch.cuda.synchronize()
+    return sets
+
+
+def timed_steps(step, steps, warmup):
+    """Wall time per step over `steps` calls, and the mean device time of each
+    stage from the events the library recorded inside those same calls."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    for _ in range(warmup):
+        step()
+    sets = stage_event_sets(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for evs in sets:
+        step([e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / steps
+    stage_ms = [sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in sets) / steps
+                for i in range(dsa.DSA_NUM_STAGES)]
+    return ms_step, stage_ms
+
+
+def wall_ms(fn, iters, warmup=2):
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
+    t0 = time.perf_counter()
     for _ in range(iters):
         fn()
+    torch.cuda.synchronize()
+    return 1e3 * (time.perf_counter() - t0) / iters
+
+
+def copy_bandwidth(gib=2, iters=10):
+    """HBM bandwidth of a plain device-to-device copy (read + write bytes)."""
+    import torch
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    s.record()
+    for _ in range(iters):
+        dst.copy_(src)
     e.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters
+    gbs = 2 * n * iters / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def cpu_baseline(batch, rows, threads):
@@ -58,6 +230,59 @@ def cpu_baseline(batch, rows, threads):
     return time.perf_counter() - t0
 
 
+def prefill_measure(steps):
+    """Prefill-chunk form: the indexer as a dense causal FP8 contraction."""
+    import torch
+
+    import synth
+    from sparse_attention_02_amd import accounting
+    from synth.device import to_device
+    b = synth.make_workload(PREFILL_WORKLOAD)
+    d = to_device(b)
+    step = Step(b, d)
+    ms_step, stage_ms = timed_steps(step, steps, 2)
+    work = accounting.batch_work(b.seqlens_k, b.n_q)
+    tflops = work["indexer_flops"] / (stage_ms[0] * 1e-3) / 1e12
+    res = {"workload": b.name, "query_rows": b.T, "ms_per_step": ms_step,
+           "stages_ms": dict(zip(("index_score", "topk", "attention"), stage_ms)),
+           "indexer_fp8_tflops": tflops, "indexer_mfma_frac": tflops / FP8_PEAK_TFLOPS,
+           "attention_bf16_tflops": work["mla_flops"] / (stage_ms[2] * 1e-3) / 1e12}
+    del step, d
+    torch.cuda.empty_cache()
+    return res
+
+
+def mli_measure(steps):
+    """Two-stream MLI step vs the same kernels back to back on one stream."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    import synth
+    from synth.device import to_device
+    b = synth.make_workload(MLI_WORKLOAD)
+    d = to_device(b)
+    first = Step(b, d, layer=0)
+    first()
+    # one stream: layer 1's indexer + top-k, then attention (layer 0's latent)
+    seq = Step(b, d, layer=1, mla_layer=0)
+    # two streams: the attention reads layer 0's selection while layer 1's
+    # indexer + top-k run beside it
+    mli = Step(b, d, mode=dsa.DSA_MODE_MLI, attend_idx=first.idx, layer=1, mla_layer=0)
+    ms_seq = wall_ms(seq, steps)
+    ms_mli = wall_ms(mli, steps)
+    torch.cuda.synchronize()
+    a, c = first.idx.cpu().numpy(), mli.idx.cpu().numpy()
+    ov = [len(np.intersect1d(a[i][a[i] >= 0], c[i][c[i] >= 0])) / max(1, int((a[i] >= 0).sum()))
+          for i in range(b.T)]
+    res = {"workload": b.name, "query_rows": b.T, "ms_one_stream": ms_seq,
+           "ms_two_streams": ms_mli, "speedup": ms_seq / ms_mli,
+           "overlap_mean": float(np.mean(ov)), "overlap_min": float(np.min(ov))}
+    del first, seq, mli, d
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -65,13 +290,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--extras", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DSA decode path here runs on a single "
               "MI355X (no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import sparse_attention_02_amd as dsa
@@ -81,51 +312,25 @@ def main():
 
     dsa.lib()
     t0 = time.perf_counter()
-    b = synth.make_workload(WORKLOAD)
+    b = synth.make_workload(DECODE_WORKLOAD)
     log(f"generated {b.name} in {time.perf_counter() - t0:.1f}s")
     d = to_device(b)
     torch.cuda.synchronize()
-    k, T = synth.TOPK, b.T
-    ws_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_DECODE_STEP, d.meta, k)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    out = torch.empty((T, 128, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((T, 128), dtype=torch.float32, device="cuda")
-    ix = dict(q8=d.q8, q_scale=d.q_scale, w=d.w, k8_cache=d.k8[0], k_scale=d.k_scale[0])
-    ml = dict(q=d.q[0], kv_cache=d.kv[0], sm_scale=synth.SM_SCALE)
-
-    def step():
-        dsa.dsa_decode_step(d.meta, ix, ml, k, dsa.DSA_MODE_FUSED, 0, None, idx, out, lse, ws,
-                            ws_bytes)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_step = 1e3 * elapsed / args.steps
-    log(f"step {ms_step:.3f} ms")
-
-    # dominant kernel: the indexer scan, timed alone by HIP events on its stream
-    ld = (b.max_seqlen_k + 63) // 64 * 64
-    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
-    ms_idx = time_stream(lambda: dsa.dsa_index_score(d.meta, d.q8, d.q_scale, d.w, d.k8[0],
-                                                     d.k_scale[0], scores, ld), 20)
-    tk_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, d.meta, k)
-    ms_topk = time_stream(lambda: dsa.dsa_topk(d.meta, scores, ld, k, idx, ws, tk_bytes), 20)
-    mla_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, d.meta, k, 0)
-    ms_mla = time_stream(lambda: dsa.dsa_sparse_mla_decode(d.meta, d.q[0], d.kv[0], idx, k,
-                                                           synth.SM_SCALE, out, lse, 0, ws,
-                                                           mla_bytes), 20)
+    step = Step(b, d)
+    ms_step, (ms_idx, ms_topk, ms_attn) = timed_steps(step, args.steps, args.warmup)
+    T = b.T
     work = accounting.batch_work(b.seqlens_k, b.n_q)
     idx_gbs = work["indexer_bytes"] / (ms_idx * 1e-3) / 1e9
-    attn_gbs = work["attention_bytes"] / (ms_mla * 1e-3) / 1e9
+    traffic = recorded_traffic()
+    attn_gbs = work["attention_bytes"] / (ms_attn * 1e-3) / 1e9
     step_gbs = work["bytes"] / (ms_step * 1e-3) / 1e9
-    log(f"indexer {ms_idx:.3f} ms {idx_gbs:.0f} GB/s | top-k {ms_topk:.3f} ms | "
-        f"attention {ms_mla:.3f} ms {attn_gbs:.0f} GB/s | step {step_gbs:.0f} GB/s")
+    log(f"step {ms_step:.3f} ms | indexer {ms_idx:.3f} ms {idx_gbs:.0f} GB/s | top-k "
+        f"{ms_topk:.3f} ms | attention {ms_attn:.3f} ms {attn_gbs:.0f} GB/s | step "
+        f"{step_gbs:.0f} GB/s")
+    del step, d
+    torch.cuda.empty_cache()
+    copy_gbs = copy_bandwidth()
+    log(f"device copy {copy_gbs:.0f} GB/s")
 
     result = {
         "metric": METRIC,
@@ -141,17 +346,23 @@ def main():
         "dtype": "fp8+bf16",
         "data": "synthetic",
         "config": {"workload": b.name, "requests": b.B, "query_rows": T,
-                   "context": int(b.max_seqlen_k), "topk": k, "page_size": 64,
+                   "context": int(b.max_seqlen_k), "topk": synth.TOPK, "page_size": 64,
                    "indexer": "64x128 fp8", "mla": "128 heads x 576 bf16"},
         "step_hbm": {"algorithmic_bytes": work["bytes"], "achieved_gbs": step_gbs,
-                     "frac": step_gbs / HBM_PEAK_GBS},
-        "stages_ms": {"index_score": ms_idx, "topk": ms_topk, "sparse_mla": ms_mla},
+                     "frac": step_gbs / HBM_PEAK_GBS, "device_copy_gbs": copy_gbs},
+        "stages_ms": {"index_score": ms_idx, "topk": ms_topk, "attention": ms_attn},
         "roofline": {"kernel": "index_score_kernel", "bound": "hbm", "achieved": idx_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": idx_gbs / HBM_PEAK_GBS,
-                     "traffic": None},
-        "attention_roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS},
+                     "traffic": traffic, "algorithmic_bytes": work["indexer_bytes"]},
+        "attention_roofline": {"kernel": "sparse_mla_kernel + mla_merge_kernel", "bound": "hbm",
+                               "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": attn_gbs / HBM_PEAK_GBS},
     }
+    if args.extras:
+        result["prefill"] = prefill_measure(max(3, args.steps // 10))
+        log(f"prefill {result['prefill']}")
+        result["mli"] = mli_measure(max(5, args.steps // 2))
+        log(f"mli {result['mli']}")
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         rows = list(range(min(args.cpu_rows, T)))

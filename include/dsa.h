@@ -166,10 +166,23 @@ typedef enum {
   DSA_MODE_MLI = 1
 } dsa_step_mode;
 
+/* Stages of a step, in the order of the optional stage events. */
+enum {
+  DSA_STAGE_INDEX_SCORE = 0, /* the indexer scan kernel */
+  DSA_STAGE_TOPK = 1,        /* top-k selection after the scan */
+  DSA_STAGE_ATTENTION = 2,   /* sparse MLA and its split merge */
+  DSA_NUM_STAGES = 3
+};
+
 typedef struct {
   int32_t mode;               /* dsa_step_mode */
   int32_t n_split;            /* as dsa_sparse_mla_decode (0 = choose) */
   const int32_t* attend_idx;  /* MLI: int32 [T, k] selection the attention reads */
+  /* Optional (NULL = none): 2 * DSA_NUM_STAGES caller-created hipEvent_t.
+   * Event 2i is recorded just before stage i and event 2i+1 just after it,
+   * on the stream that stage runs on, so hipEventElapsedTime over the pair
+   * is that stage's device time.  The caller owns the events. */
+  void* const* stage_events;
 } dsa_step_opts_t;
 
 /* One decode step of one layer: indexer scores, top-k, sparse MLA.

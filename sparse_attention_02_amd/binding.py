@@ -16,6 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so"
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP = 1, 2, 3
 DSA_MODE_FUSED, DSA_MODE_MLI = 0, 1
+DSA_STAGE_INDEX_SCORE, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_NUM_STAGES = 0, 1, 2, 3
 PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 128, 128, 576, 512, 8192
 
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
@@ -48,7 +49,7 @@ class dsa_mla_inputs_t(ctypes.Structure):
 
 class dsa_step_opts_t(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_split", ctypes.c_int32),
-                ("attend_idx", ctypes.c_void_p)]
+                ("attend_idx", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -158,12 +159,19 @@ def dsa_sparse_mla_decode(batch: Batch, q, kv_cache, idx, k: int, sm_scale: floa
 
 def dsa_decode_step(batch: Batch, ix: dict, mla: dict, k: int, mode: int, n_split: int,
                     attend_idx, idx_out, out, lse, ws, ws_bytes: int, stream_main=None,
-                    stream_aux=None):
-    """ix: q8, q_scale, w, k8_cache, k_scale; mla: q, kv_cache, sm_scale."""
+                    stream_aux=None, stage_events=None):
+    """ix: q8, q_scale, w, k8_cache, k_scale; mla: q, kv_cache, sm_scale.
+    stage_events: None or 2 * DSA_NUM_STAGES raw hipEvent_t handles (ints)."""
+    evs = None
+    if stage_events is not None:
+        if len(stage_events) != 2 * DSA_NUM_STAGES or not all(stage_events):
+            raise ValueError(f"stage_events needs {2 * DSA_NUM_STAGES} event handles")
+        evs = (ctypes.c_void_p * len(stage_events))(*stage_events)
     ixs = dsa_indexer_inputs_t(_ptr(ix["q8"]), _ptr(ix["q_scale"]), _ptr(ix["w"]),
                                _ptr(ix["k8_cache"]), _ptr(ix["k_scale"]))
     ms = dsa_mla_inputs_t(_ptr(mla["q"]), _ptr(mla["kv_cache"]), float(mla["sm_scale"]))
-    opts = dsa_step_opts_t(int(mode), int(n_split), _ptr(attend_idx))
+    opts = dsa_step_opts_t(int(mode), int(n_split), _ptr(attend_idx),
+                           None if evs is None else ctypes.cast(evs, ctypes.c_void_p))
     aux = None if stream_aux is None else _stream(stream_aux)
     _check(lib().dsa_decode_step(batch.ref(), ctypes.byref(ixs), ctypes.byref(ms), int(k),
                                  ctypes.byref(opts), _ptr(idx_out), _ptr(out), _ptr(lse),

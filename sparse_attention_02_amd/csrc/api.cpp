@@ -235,25 +235,40 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
 
   // indexer + top-k on stream s: the scan also builds the first radix
   // histogram of each row, so the top-k starts at its threshold step
+  // optional stage events: mark(i, 0) before stage i, mark(i, 1) after it
+  auto mark = [&](int stage, int end, hipStream_t s) -> hipError_t {
+    if (!opts->stage_events) return hipSuccess;
+    return hipEventRecord((hipEvent_t)opts->stage_events[2 * stage + end], s);
+  };
+
   auto select = [&](hipStream_t s) -> int {
     hipError_t e = dsa::launch_topk_zero(a, topk_ws, s);
     if (e != hipSuccess) return hip_fail(e, "top-k zero launch");
+    if ((e = mark(DSA_STAGE_INDEX_SCORE, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
                                 ld, dsa::topk_hist1(a, topk_ws), s);
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
+    if ((e = mark(DSA_STAGE_INDEX_SCORE, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = mark(DSA_STAGE_TOPK, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = dsa::launch_topk_select(a, scores, ld, k, idx_out, topk_ws, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    if ((e = mark(DSA_STAGE_TOPK, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return DSA_OK;
+  };
+  auto attend = [&](const int32_t* sel) -> int {
+    hipError_t e = mark(DSA_STAGE_ATTENTION, 0, sm);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, sel, k, mla->sm_scale, out, lse, used,
+                               mla_ws, sm);
+    if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+    if ((e = mark(DSA_STAGE_ATTENTION, 1, sm)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return DSA_OK;
   };
 
   if (!mli) {
     rc = select(sm);
     if (rc) return rc;
-    hipError_t e;
-    e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, idx_out, k, mla->sm_scale, out, lse,
-                               used, mla_ws, sm);
-    if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
-    return DSA_OK;
+    return attend(idx_out);
   }
 
   // MLI: attention over the previous indexer layer's selection on the main
@@ -268,9 +283,8 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   rc = select(sa);
   if (rc) return rc;
-  e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, opts->attend_idx, k, mla->sm_scale, out,
-                             lse, used, mla_ws, sm);
-  if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+  rc = attend(opts->attend_idx);
+  if (rc) return rc;
   e = hipEventRecord(ev_done, sa);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = hipStreamWaitEvent(sm, ev_done, 0);

@@ -140,3 +140,24 @@ def test_workspace_sizes_grow_with_the_batch(L):
             L.dsa_workspace_size(op, ctypes.byref(small), 64, 0)
     assert L.dsa_workspace_size(99, ctypes.byref(small), 64, 0) == 0
     assert L.dsa_default_splits(ctypes.byref(small), 2048) == 64
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("DSA_MODE_FUSED", "DSA_MODE_MLI", "DSA_STAGE_INDEX_SCORE", "DSA_STAGE_TOPK",
+                 "DSA_STAGE_ATTENTION", "DSA_NUM_STAGES", "DSA_OP_TOPK", "DSA_OP_SPARSE_MLA",
+                 "DSA_OP_DECODE_STEP"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name), name
+
+
+def test_step_opts_layout():
+    # mode, n_split, attend_idx, stage_events: 4 + 4 + 8 + 8 bytes
+    assert ctypes.sizeof(B.dsa_step_opts_t) == 24
+    assert B.dsa_step_opts_t.stage_events.offset == 16
+
+
+def test_stage_events_argument_checked():
+    with pytest.raises(ValueError):
+        B.dsa_decode_step(None, {}, {}, 16, 0, 0, None, None, None, None, None, 0,
+                          stage_events=[1, 2, 3])
