@@ -18,6 +18,8 @@
 // its rows.  With HIST the epilogue also counts each score's top-11-bit key
 // digit into an LDS histogram per row, added to the row's global histogram
 // at the end (the first radix pass of the top-k, without re-reading scores).
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace dsa {
@@ -25,7 +27,23 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 16;  // pages per work-group
+constexpr int kChunk = 16;  // pages per work-group of the row-group form
+#ifndef DSA_SCAN_TARGET_WGS
+#define DSA_SCAN_TARGET_WGS 2048
+#endif
+#ifndef DSA_SCAN_NPF1
+#define DSA_SCAN_NPF1 2
+#endif
+#ifndef DSA_SCAN_NPF2
+#define DSA_SCAN_NPF2 2
+#endif
+constexpr int kScanTargetWGs = DSA_SCAN_TARGET_WGS;
+constexpr int kScanNPF1 = DSA_SCAN_NPF1;
+constexpr int kScanNPF2 = DSA_SCAN_NPF2;
+#ifndef DSA_SCAN_STAGE_PAGES
+#define DSA_SCAN_STAGE_PAGES 64
+#endif
+constexpr int kStagePages = DSA_SCAN_STAGE_PAGES;  // most pages per work-group
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -192,21 +210,251 @@ hipError_t launch_rg(dim3 grid, hipStream_t s, const BatchArgs& b, const uint8_t
   return hipGetLastError();
 }
 
+// ---- decode form: one wave per page ------------------------------------
+//
+// For requests of at most two query rows (a decode token, plus one MTP
+// draft) each key page is scanned by one wave on its own.  The page's 64
+// keys are the four 16-key column tiles of the MFMA, so after the ReLU * w
+// reduction over heads the 64 lanes hold the page's 64 scores in order and
+// each row's scores leave in one 256-byte store.  The cross-lane part of the
+// head reduction is a reduce-scatter over the four 16-lane rows with the
+// permlane32 / permlane16 swaps, with no LDS.  Keys arrive through buffer
+// loads whose descriptor spans exactly one page: a page past the wave's range
+// or with an id outside the pool gets a zero-size descriptor, so its loads
+// return zeros without touching memory and nothing is stored for it.
+constexpr int kPageWaves = 4;
+constexpr int kPageKeyBytes = DSA_PAGE_SIZE * DSA_IDX_DIM;
+constexpr int kBufNT = 2;  // nontemporal cache policy of a buffer load
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// lane (j, g) holds p[c] for column tile c, summed over its own heads; the
+// result in lane (j, g) is the sum over all four g of column tile g
+__device__ __forceinline__ float reduce_scatter4(const float p[4]) {
+  const v2u a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]),
+                                                 false, false);
+  const v2u c = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]),
+                                                 false, false);
+  const float x = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // tile 0 | tile 2
+  const float y = __uint_as_float(c[0]) + __uint_as_float(c[1]);  // tile 1 | tile 3
+  const v2u d = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                 false);
+  return __uint_as_float(d[0]) + __uint_as_float(d[1]);
+}
+
+template <int RG, int NPF, bool HIST>
+__global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
+    BatchArgs b, const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k8,
+    const float* __restrict__ k_scale, float* __restrict__ scores, int64_t ld,
+    uint32_t* __restrict__ hist, int chunk_pages) {
+  __shared__ uint32_t lh[HIST ? RG * kTopkBins : 1];
+  // the work-group's scores, written out in one burst at the end
+  __shared__ float lsc[RG][kStagePages * DSA_PAGE_SIZE];
+  const int chunk = blockIdx.x;
+  const int bi = blockIdx.y;
+  const int c0 = b.cu[bi];
+  const int n = b.cu[bi + 1] - c0;  // 0 .. RG rows (the launch checks max_q <= RG)
+  if (n <= 0 || n > RG) return;
+  const int L = clamp_len(b, b.lens[bi]);
+  const int p_begin = chunk * chunk_pages;
+  const int p_end = min(p_begin + chunk_pages, (L + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE);
+  if (p_begin >= p_end) return;
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (readfirstlane tells the compiler so: the page descriptors
+  // built from it then stay in scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  if (HIST) {
+    for (int i = threadIdx.x; i < RG * kTopkBins; i += kThreads) lh[i] = 0u;
+  }
+
+  // the wave's pages are p_begin + wave + 4i, i < np (np <= 64: one id per lane)
+  const int np = max(0, (p_end - p_begin - wave + kPageWaves - 1) / kPageWaves);
+  const int32_t* ptab = b.pages + (int64_t)bi * b.max_pages;
+  const int my_pid = lane < np ? ptab[p_begin + wave + kPageWaves * lane] : -1;
+  auto page_id = [&](int i) { return i < np ? __builtin_amdgcn_readlane(my_pid, i) : -1; };
+  auto page_ok = [&](int pg) { return pg >= 0 && pg < b.num_pages; };
+
+  // A operands and weights of each row (rows past the request's last repeat it)
+  v8i qf[RG][4];
+  float wr[RG][4][4];
+  float qs[RG];
+  int vis[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int t = c0 + min(r, n - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      qf[r][m] = load_frag(q8 + ((int64_t)t * DSA_IDX_HEADS + 16 * m + j) * DSA_IDX_DIM + 32 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wr[r][m][e] = w[(int64_t)t * DSA_IDX_HEADS + 16 * m + 4 * g + e];
+    }
+    qs[r] = q_scale[t];
+    vis[r] = r < n ? min(L, max(0, L - n + 1 + r)) : 0;
+  }
+
+  // key ring: NPF pages in flight per wave.  Page i + NPF is loaded into
+  // the registers of page i tile by tile, right after that tile's MFMAs have
+  // read them, so no register of the ring is ever copied (a copy would wait
+  // for the load in flight).
+  const int koff = j * DSA_IDX_DIM + 32 * g;  // + 2048 c for column tile c
+  v8i kf[NPF][4];
+  float ksr[NPF];
+  int pgr[NPF];
+  auto key_rsrc = [&](int pg) {
+    const bool ok = page_ok(pg);
+    return page_rsrc(k8 + (int64_t)(ok ? pg : 0) * kPageKeyBytes, ok ? kPageKeyBytes : 0);
+  };
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t kr, int c) {
+    // column tile c's offset rides in the scalar offset, so all tiles share
+    // one address register
+    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 2048 * c, kBufNT);
+    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16, 2048 * c, kBufNT);
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+  auto load_scale = [&](int pg) {
+    const bool ok = page_ok(pg);
+    const __amdgpu_buffer_rsrc_t sr = page_rsrc(
+        k_scale + (int64_t)(ok ? pg : 0) * DSA_PAGE_SIZE, ok ? DSA_PAGE_SIZE * 4 : 0);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, 4 * lane, 0, kBufNT));
+  };
+#pragma unroll
+  for (int u = 0; u < NPF; ++u) {
+    pgr[u] = page_id(u);
+    const __amdgpu_buffer_rsrc_t kr = key_rsrc(pgr[u]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kf[u][c] = load_tile(kr, c);
+    ksr[u] = load_scale(pgr[u]);
+  }
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  for (int i0 = 0; i0 < np; i0 += NPF) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int i = i0 + u;
+      const int pg = pgr[u];
+      const int nx = page_id(i + NPF);
+      const __amdgpu_buffer_rsrc_t nr = key_rsrc(nx);
+      // every wave runs whole groups of NPF pages; past np the pages are
+      // zero-size (their loads read nothing) and nothing is stored
+      float part[RG][4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v4f acc[RG][4];
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[r][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[r][m], kf[u][c], zero, 0,
+                                                                      0, 0, 0, 0, 0);
+        // the next page's tile c reuses this tile's registers: keep the
+        // scheduler from hoisting the loads above the MFMAs that read them
+        __builtin_amdgcn_sched_barrier(0);
+        kf[u][c] = load_tile(nr, c);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          float sum = 0.f;
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum = fmaf(wr[r][m][e], relu(acc[r][m][e]), sum);
+          part[r][c] = sum;
+        }
+        // one tile's MFMA results live at a time (the other waves of the
+        // SIMD overlap their MFMAs with this epilogue)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int lp = wave + kPageWaves * i;  // page within the work-group's range
+      const int pos = (p_begin + lp) * DSA_PAGE_SIZE + lane;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const float tot = reduce_scatter4(part[r]);
+        if (page_ok(pg) && r < n && pos < vis[r]) {
+          const float sc = tot * qs[r] * ksr[u];
+          lsc[r][lp * DSA_PAGE_SIZE + lane] = sc;
+          if (HIST) atomicAdd(&lh[r * kTopkBins + (float_key(sc) >> 21)], 1u);
+        }
+      }
+      ksr[u] = load_scale(nx);
+      pgr[u] = nx;
+    }
+  }
+
+  __syncthreads();
+  // scores of the range, row by row: positions below the row's visible count
+  // on pages with a valid id, in 16-byte stores where the row is aligned.
+  // The stores are nontemporal: written while the key stream is being read,
+  // cached writes cost the scan far more than their share of the bytes.
+  const int base = p_begin * DSA_PAGE_SIZE;
+  const int span = (p_end - p_begin) * DSA_PAGE_SIZE;
+  for (int r = 0; r < n; ++r) {
+    const int lim = min(span, vis[r] - base);
+    float* row = scores + (int64_t)(c0 + r) * ld + base;
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    for (int x = 4 * threadIdx.x; x < lim; x += 4 * kThreads) {
+      if (!page_ok(ptab[p_begin + x / DSA_PAGE_SIZE])) continue;
+      if (vec && x + 4 <= lim) {
+        __builtin_nontemporal_store(*reinterpret_cast<const v4f*>(&lsc[r][x]),
+                                    reinterpret_cast<v4f*>(row + x));
+      } else {
+        for (int e = 0; e < 4 && x + e < lim; ++e) __builtin_nontemporal_store(lsc[r][x + e], row + x + e);
+      }
+    }
+  }
+  if (HIST) {
+    for (int i = threadIdx.x; i < n * kTopkBins; i += kThreads) {
+      const uint32_t c = lh[i];
+      if (c) atomicAdd(&hist[(int64_t)(c0 + i / kTopkBins) * kTopkBins + (i % kTopkBins)], c);
+    }
+  }
+}
+
+template <int RG, int NPF>
+hipError_t launch_page(int chunk_pages, int chunks, hipStream_t s, const BatchArgs& b,
+                       const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
+                       const float* k_scale, float* scores, int64_t ld, uint32_t* hist) {
+  const dim3 grid(chunks, b.B);
+  if (hist)
+    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, true>), grid, dim3(kThreads), 0, s, b,
+                       q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
+  else
+    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, false>), grid, dim3(kThreads), 0, s, b,
+                       q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float* q_scale,
                               const float* w, const uint8_t* k8, const float* k_scale,
                               float* scores, int64_t ld, uint32_t* hist, hipStream_t s) {
   if (b.B == 0 || b.T == 0 || b.max_seqlen_k == 0) return hipSuccess;
-  const int rg = b.max_q <= 1 ? 1 : (b.max_q <= 2 ? 2 : 4);
-  const int groups = (b.max_q + rg - 1) / rg;
   const int total_pages = (b.max_seqlen_k + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE;
+  if (b.max_q <= 2) {
+    // pages per work-group: about kScanTargetWGs work-groups over the batch
+    // (sized for its longest request), at most 64 pages per wave
+    const int64_t all = (int64_t)total_pages * b.B;
+    int cp = (int)std::min<int64_t>(kStagePages, (all + kScanTargetWGs - 1) / kScanTargetWGs);
+    cp = std::max(kPageWaves, (cp + kPageWaves - 1) / kPageWaves * kPageWaves);
+    const int chunks = (total_pages + cp - 1) / cp;
+    if (b.max_q <= 1)
+      return launch_page<1, kScanNPF1>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores, ld,
+                                       hist);
+    return launch_page<2, kScanNPF2>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores, ld,
+                                     hist);
+  }
+  const int groups = (b.max_q + 3) / 4;
   const int chunks = (total_pages + kChunk - 1) / kChunk;
   dim3 grid(groups, chunks, b.B);
-  if (rg == 1)
-    return launch_rg<1, 8, true>(grid, s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist);
-  if (rg == 2)
-    return launch_rg<2, 4, true>(grid, s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist);
   if (groups == 1)
     return launch_rg<4, 2, true>(grid, s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist);
   return launch_rg<4, 2, false>(grid, s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist);
