@@ -95,7 +95,9 @@ typedef struct {
  *  k_scale  f32 [num_pages, 64]    one positive scale per cached key
  *  scores   f32 [T, ld] out: scores[t, s] = q_scale[t] * k_scale[slot(s)] *
  *           sum_h w[t,h] * max(0, sum_d e4m3(q8[t,h,d]) * e4m3(k8[slot(s),d]))
- *           for s < v_t (row t's visible length); entries s >= v_t are not written.
+ *           for s < v_t (row t's visible length); entries s >= v_t are not
+ *           written, nor are the positions of a page whose id is outside
+ *           [0, num_pages) (the pool holds no key for them).
  *           With positive scales this equals I(t,s) on the dequantised values.
  *  ld       >= max_seqlen_k
  * Errors: INVALID_ARG (null pointers with T > 0, ld too small, bad scalars). */
@@ -109,10 +111,8 @@ int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_
  *  k       1 .. DSA_MAX_TOPK
  *  idx     int32 [T, k] out: the K_t = min(k, v_t) selected logical positions
  *          (ties at the k-th score go to the lower position), stored in
- *          idx[t, 0 .. K_t), followed by -1 in idx[t, K_t .. k).  Order within
- *          the K_t entries: first every position whose score is above the
- *          threshold bucket, ascending, then the rest, ascending; it is
- *          deterministic.
+ *          idx[t, 0 .. K_t) in ascending order, followed by -1 in
+ *          idx[t, K_t .. k); the output is deterministic.
  *  ws      device workspace of >= dsa_workspace_size(DSA_OP_TOPK, ...) bytes
  * Errors: INVALID_ARG, WORKSPACE. */
 int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,

@@ -227,13 +227,20 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
     const uint32_t mask = tile_mask[tile];
     float z[8];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[r] = (mask >> (4 * g + r)) & 1u ? s0[r] * scale_log2 : -INFINITY;
-      z[4 + r] = (mask >> (16 + 4 * g + r)) & 1u ? s1[r] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, fmaxf(z[r], z[4 + r]));
+      z[r] = s0[r] * scale_log2;
+      z[4 + r] = s1[r] * scale_log2;
     }
+    if (mask != 0xffffffffu) {  // a tile with skipped tokens (rare)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!((mask >> (4 * g + r)) & 1u)) z[r] = -INFINITY;
+        if (!((mask >> (16 + 4 * g + r)) & 1u)) z[4 + r] = -INFINITY;
+      }
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
@@ -251,7 +258,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      p[r] = m_ref == -INFINITY ? 0.f : exp2f(z[r] - m_ref);
+      p[r] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
       psum += p[r];
     }
     l_run += psum;

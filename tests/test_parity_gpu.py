@@ -58,6 +58,52 @@ def test_index_score_small(ci):
         assert np.isnan(g[i, v:]).all()
 
 
+# SMALL cases with at most two rows per request (the scan form that gives
+# each key page to one wave)
+PAGE_FORM = [0, 1, 2, 5]
+
+
+@pytest.mark.parametrize("ci", PAGE_FORM)
+def test_index_score_unaligned_row_stride(ci):
+    """ld not a multiple of 4: rows start unaligned and the scan writes them
+    out element by element; nothing past a row's visible length is touched."""
+    b = _small(SMALL[ci], 150 + ci)
+    d = to_device(b)
+    scores, ld = index_scores(d, ld=int(b.max_seqlen_k) + 5)
+    sync()
+    meta, vis, sc, *_ = oracle_rows(b, list(range(b.T)))
+    got = scores.cpu().numpy().astype(np.float64)
+    check_scores(got, sc, vis)
+    for i, v in enumerate(vis):
+        assert np.all(np.isnan(got[i, v:])), i
+
+
+@pytest.mark.parametrize("case", [dict(n_q=[2, 1], L=[5000, 3000]), dict(n_q=[1], L=[3000]),
+                                  dict(n_q=[3, 1], L=[4000, 2500])])
+def test_index_score_leaves_pages_with_invalid_ids_unwritten(case):
+    b = _small(case, 160)
+    meta, vis, sc, *_ = oracle_rows(b, list(range(b.T)))
+    bad = b.page_table.copy()
+    bad[0, 1] = -1
+    bad[0, 3] = b.num_pages + 7
+    if b.B > 1:
+        bad[1, 0] = -5
+    b.page_table = bad
+    d = to_device(b)
+    scores, ld = index_scores(d)
+    sync()
+    got = scores.cpu().numpy().astype(np.float64)
+    cu = b.cu_seqlens_q
+    for r in range(b.B):
+        for t in range(cu[r], cu[r + 1]):
+            for pg in np.nonzero((bad[r] < 0) | (bad[r] >= b.num_pages))[0]:
+                lo, hi = 64 * pg, min(64 * pg + 64, vis[t])
+                if lo < hi:
+                    assert np.all(np.isnan(got[t, lo:hi])), (t, pg)
+                    got[t, lo:hi] = sc[t, lo:hi]
+    check_scores(got, sc, vis)
+
+
 @pytest.mark.parametrize("ci", range(len(SMALL)))
 @pytest.mark.parametrize("k", [1, 37, 2048])
 def test_topk_small_exact_on_same_scores(ci, k):
