@@ -37,7 +37,7 @@ DECODE_WORKLOAD = 2
 PREFILL_WORKLOAD = 3
 MLI_WORKLOAD = 4
 PROFILES = os.path.join(ROOT, "profiles")
-COUNTERS_SUMMARY = os.path.join(PROFILES, "counters.index_score_kernel.decode-b64-mtp1-ctx131072.md")
+COUNTERS_SUMMARY = os.path.join(PROFILES, "counters.decode-step.decode-b64-mtp1-ctx131072.md")
 # the sources that make up the indexer scan kernel: its counters describe it
 # only while these are unchanged
 INDEXER_SOURCES = ["sparse_attention_02_amd/csrc/indexer.hip",
@@ -112,7 +112,7 @@ def summarize_counters(fetch_dir, write_dir):
         wk = vals["WRITE_SIZE"].get(k, (0, 0.0))[1]
         hbm = 1024 * (FETCH_SCALE * fk + WRITE_SCALE * wk)
         print(f"| {k} | {n} | {fk:.0f} | {wk:.0f} | {hbm:.4g} |")
-        if k.startswith("index_score_kernel"):
+        if k.startswith("index_score"):
             idx = hbm
     print(f"\nfetch_scale: {FETCH_SCALE}\nwrite_scale: {WRITE_SCALE}")
     if idx is not None:
@@ -351,7 +351,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": work["bytes"], "achieved_gbs": step_gbs,
                      "frac": step_gbs / HBM_PEAK_GBS, "device_copy_gbs": copy_gbs},
         "stages_ms": {"index_score": ms_idx, "topk": ms_topk, "attention": ms_attn},
-        "roofline": {"kernel": "index_score_kernel", "bound": "hbm", "achieved": idx_gbs,
+        "roofline": {"kernel": "index_score_page_kernel", "bound": "hbm", "achieved": idx_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": idx_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": work["indexer_bytes"]},
         "attention_roofline": {"kernel": "sparse_mla_kernel + mla_merge_kernel", "bound": "hbm",
