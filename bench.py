@@ -5,10 +5,10 @@ absorbed-MLA split-KV decode + LSE merge) over the decode batch of 64
 requests x 2 query rows (1 + MTP) at a 131072-token context, on seeded
 synthetic inputs resident in HBM.  Prints one JSON line.
 
-Inside the timed steps the library records HIP events around each stage
-on the stream the stage runs on; the roofline of the dominant kernel (the
-indexer scan) is its algorithmic bytes over the average of those per-launch
-durations.
+The step time comes from K back-to-back steps; then K more steps run with
+the library recording HIP events around each stage on the stream the stage
+runs on, and the roofline of the dominant kernel (the indexer scan) is its
+algorithmic bytes over the average of those per-launch durations.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extras]
   python bench.py --summarize-trace DIR            (rocprofv3 --kernel-trace --stats output)
@@ -163,20 +163,27 @@ def stage_event_sets(n):
 
 
 def timed_steps(step, steps, warmup):
-    """Wall time per step over `steps` calls, and the mean device time of each
-    stage from the events the library recorded inside those same calls."""
+    """Wall time per step over `steps` back-to-back calls, then the mean
+    device time of each stage from HIP events that the library records
+    around the stages inside a second run of `steps` calls.  (The event
+    records cost the step time of their own, so the step time is taken from
+    the run without them.)"""
     import torch
 
     import sparse_attention_02_amd as dsa
     for _ in range(warmup):
         step()
-    sets = stage_event_sets(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / steps
+    sets = stage_event_sets(steps)
+    torch.cuda.synchronize()
     for evs in sets:
         step([e.cuda_event for e in evs])
     torch.cuda.synchronize()
-    ms_step = 1e3 * (time.perf_counter() - t0) / steps
     stage_ms = [sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in sets) / steps
                 for i in range(dsa.DSA_NUM_STAGES)]
     return ms_step, stage_ms

@@ -181,6 +181,29 @@ def test_sparse_mla_small_oracle_selection(ci, n_split, stress):
     check_attention(bf16_to_f64(out), ref, lse.cpu().numpy(), ref_lse, relative=not stress)
 
 
+@pytest.mark.parametrize("n_split", [1, 3])
+def test_sparse_mla_wide_logit_range(n_split):
+    """Queries scaled by 2^6: logits spread over hundreds of units, so later
+    tiles exceed the first tile's maximum by far more than the kernel lets
+    its softmax weights grow, and it must take the exact maximum and start
+    again."""
+    b = _small(dict(n_q=[2, 1], L=[6000, 2500]), 650, mla_scale=1.0)
+    q = b.q[0]
+    f = (q.astype(np.uint32) << 16).view(np.float32) * np.float32(64.0)
+    b.q[0] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    d = to_device(b)
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, list(range(b.T)))
+    idx = torch.from_numpy(sel).cuda()
+    out, lse = sparse_mla(d, idx, n_split=n_split)
+    sync()
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], sel, list(range(b.T)), synth.SM_SCALE)
+    assert np.abs(ref_lse[np.isfinite(ref_lse)]).max() > 100  # the case is wide
+    check_attention(bf16_to_f64(out), ref, relative=False)
+    # lse ~ a few hundred: fp32 sums of 576 products carry ~1e-6 relative
+    g = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(g - ref_lse).max() <= 1e-3 + 4e-6 * np.abs(ref_lse).max()
+
+
 def test_sparse_mla_split_invariance_and_determinism():
     b = _small(SMALL[5], 600, mla_scale=1.0)
     d = to_device(b)
