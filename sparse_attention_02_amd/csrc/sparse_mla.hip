@@ -9,23 +9,25 @@
 // "Deepseek Details", section DSA).
 //
 // One work-group (8 waves, two per SIMD) owns one (row, split) and all 128
-// heads, so each gathered latent row is read from HBM once per row.  Wave w
-// owns heads 16w .. 16w+15: its query fragment (16 heads x 576) and its
-// output accumulator (512 dims x 16 heads, fp32) stay in registers
-// (v_mfma_f32_16x16x32_bf16).  Per tile of 32 selected tokens:
+// heads, so each gathered latent row is read from HBM once per row.  Per
+// tile of 32 selected tokens:
 //   gather   slots come from a per-split table built once (position -> page
 //            -> slot); the 1152-byte rows go straight from HBM into LDS with
-//            global_load_lds_dwordx4 (row pitch 1168 bytes), double-buffered:
+//            global_load_lds_dwordx4 (row pitch 1184 bytes), double-buffered:
 //            tile i+1 streams in while tile i computes;
-//   transpose the first 512 dims into a [dim][token] copy so that the value
-//            product has its contraction (token) dim contiguous;
-//   S^T      = KV Q^T (32 tokens x 16 heads per wave);
-//   softmax  online, per head, in fp32; the reference max is only raised
-//            when a score exceeds it by 2^8, so the accumulator is rarely
-//            rescaled (the result does not depend on the reference);
-//   O^T     += V^T P^T (512 dims x 16 heads), P taken straight from the S^T
-//            accumulator layout (the token order of the transposed copy is
-//            permuted to match it).
+//   S^T      = KV Q^T, wave w taking heads 16w .. 16w+15 (v_mfma_f32_16x16x32_bf16,
+//            its query fragment of 16 heads x 576 dims held in registers);
+//   softmax  online, per head, in fp32 by the wave that owns the head; the
+//            reference max is only raised when a score exceeds it by 2^8, so
+//            the accumulator is rarely rescaled (the result does not depend
+//            on the reference).  P goes to LDS in the MFMA operand layout,
+//            with the rescale factor of each head;
+//   O^T     += V^T P^T, wave w taking latent dims 64w .. 64w+63 for all 128
+//            heads, so every value row is read from LDS once per tile rather
+//            than once per head group.  V^T comes straight from the
+//            token-major tile through transposing LDS reads
+//            (ds_read_b64_tr_b16: four tokens of one dim per lane), in the
+//            token order in which the S^T accumulator holds P.
 #include "device_common.h"
 
 namespace dsa {
@@ -40,16 +42,37 @@ constexpr int kKsPitch = 1184;                 // bytes per token row of the gat
 constexpr int kKsChunks = kKsPitch / 16;       // 74 (72 data + 2 pad)
 constexpr int kKsLoads = (kMlaTile * kKsChunks + 63) / 64;  // 37 wave-wide 1 KB loads
 constexpr int kKsBytes = kKsLoads * 1024;      // 37888
-constexpr int kVtPitch = 96;                   // bytes per latent-dim row of the transposed tile
 constexpr int kMaxChunk = 2048;                // selected tokens per split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleMargin = 8.f;          // log2 units
 
+constexpr int kDimsPerWave = DSA_MLA_DV / (kThreads / 64);  // 64
+
 union Frag {
   uint4 u;
   v8bf v;
 };
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// V^T operand of a 16-dim block: lane (l16, g) receives dim d0 + l16 of
+// tokens 4g .. 4g+3 and 16+4g .. 16+4g+3, i.e. k = 8g .. 8g+7 in the order
+// the S^T accumulator hands out P.  For the 16 lanes of group g, lane L
+// addresses token row 4g + L/4 (and 16 rows below) at dims d0 + 4(L%4).
+__device__ __forceinline__ v8bf v_frag(const unsigned char* K, int d0, int l16, int g) {
+  // the mask keeps the address provably inside the LDS window, which lets
+  // the constant part fold into the instruction offset
+  const uint32_t a =
+      (uint32_t)(uintptr_t)(K + (4 * g + (l16 >> 2)) * kKsPitch + (d0 + 4 * (l16 & 3)) * 2) &
+      0x3ffffu;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(uintptr_t)a);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(uintptr_t)(a + 16 * kKsPitch));
+  const v8s x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(v8bf, x);
+}
 
 __device__ __forceinline__ v8bf lds_frag(const unsigned char* p) {
   Frag f;
@@ -57,10 +80,25 @@ __device__ __forceinline__ v8bf lds_frag(const unsigned char* p) {
   return f.v;
 }
 
-// column of token 4q+r in a row of the transposed tile: the order in which the
-// S^T accumulator (16x16 layout: lane group g holds tokens 4g..4g+3 and
-// 16+4g..16+4g+3) hands P to the value product
-__device__ __forceinline__ int quad_pos(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
+constexpr unsigned kWaitVmAll = 0x0f70;   // vmcnt(0)
+constexpr unsigned kWaitLgkmAll = 0xc07f; // lgkmcnt(0)
+
+// Waits for every global load this wave issued, including those that write
+// LDS directly.  A builtin rather than inline assembly, so that the compiler
+// knows those writes are complete.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(kWaitVmAll); }
+
+// Work-group barrier over LDS only: each wave's LDS accesses complete before
+// it arrives, but loads still streaming into another buffer keep going
+// (__syncthreads' fence would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmAll);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <bool SPLIT>
 __global__ __launch_bounds__(kThreads)
@@ -69,11 +107,18 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
                        uint16_t* __restrict__ out, float* __restrict__ lse,
                        float* __restrict__ opart, float* __restrict__ lpart, int n_split, int chunk,
                        int n_work, int per_xcd) {
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[2][kKsBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char Vt[DSA_MLA_DV * kVtPitch];
+  // two named buffers rather than one array: the ring alternates between
+  // them at compile time, which lets the compiler see that reading one does
+  // not depend on the loads still streaming into the other
+  __shared__ __attribute__((aligned(16))) unsigned char Ks0[kKsBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Ks1[kKsBytes];
+  __shared__ __attribute__((aligned(16))) uint4 Pl[8 * 64];  // P^T fragments: [head block][lane]
+  __shared__ float alpha_l[DSA_MLA_HEADS];  // rescale factor of each head in this tile
+  __shared__ float fin_l[DSA_MLA_HEADS];    // 1 / softmax denominator of each head
   __shared__ int32_t slots[kMaxChunk];
   __shared__ int32_t tile_fb[kMaxChunk / kMlaTile];    // a valid slot of the tile, -1 if none
   __shared__ uint32_t tile_mask[kMaxChunk / kMlaTile];  // bit x: token x of the tile is valid
+  __shared__ int32_t tile_raise[kMaxChunk / kMlaTile];   // some head rescaled in the tile
 
   // consecutive work items land on the same XCD (work-groups are dealt to
   // the 8 XCDs round-robin), so the splits and the MTP rows of a request
@@ -87,6 +132,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int j0 = split * chunk;
   const int ntok = max(0, min(k, j0 + chunk) - j0);
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
+  const int nsteps = (ntiles + 1) & ~1;  // even: a padding tile has no valid token
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,7 +142,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int head = wave * 16 + l16;
 
   // position -> slot for the whole split (-1: skipped)
-  for (int i = tid; i < ntiles * kMlaTile; i += kThreads) {
+  for (int i = tid; i < nsteps * kMlaTile; i += kThreads) {
     int slot = -1;
     if (i < ntok) {
       const int s = idx[(int64_t)t * k + j0 + i];
@@ -108,7 +154,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     slots[i] = slot;
   }
   __syncthreads();
-  for (int tt = tid; tt < ntiles; tt += kThreads) {
+  for (int tt = tid; tt < nsteps; tt += kThreads) {
     int fb = -1;
     uint32_t mask = 0;
     for (int x = 0; x < kMlaTile; ++x) {
@@ -120,6 +166,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     }
     tile_fb[tt] = fb;
     tile_mask[tt] = mask;
+    tile_raise[tt] = 0;
   }
   __syncthreads();
 
@@ -138,7 +185,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
 
   // one tile: 37 wave-wide loads of 64 x 16 bytes; lane L of load n fills
   // byte 16*(64n + L) of the buffer = token (64n+L)/73, chunk (64n+L)%73
-  auto issue_gather = [&](int tile, int buf) {
+  auto issue_gather = [&](int tile, unsigned char* dst) {
     const int fb = tile_fb[tile];
     if (fb < 0) return;
     for (int n = wave; n < kKsLoads; n += kThreads / 64) {
@@ -149,153 +196,143 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
       if (slot < 0) slot = fb;  // padding lanes and skipped tokens re-read a valid row
       if (cc >= 72) cc = 0;  // pad chunks
       const uint16_t* src = kv + (int64_t)slot * DSA_MLA_DIM + cc * 8;
-      __builtin_amdgcn_global_load_lds(src, Ks[buf] + n * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
     }
   };
 
-  v4f acc[32];
+  // acc[db][hb][r] = O^T[dim 64w + 16db + 4g + r][head 16hb + l16]
+  v4f acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) acc[db][hb] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;  // reference max of this lane's head (log2 units)
   float l_run = 0.f;
+  const int d_base = kDimsPerWave * wave;
 
-  if (ntiles > 0) issue_gather(0, 0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile in Ks[buf]; every wave is done with the previous tile
-    if (tile + 1 < ntiles) issue_gather(tile + 1, buf ^ 1);
+  // one tile: K holds it, nxt receives the next one meanwhile
+  auto step = [&](int tile, const unsigned char* K, unsigned char* nxt) {
+    wait_vm_all();  // this wave's share of the tile has landed in LDS
+    lds_barrier();  // every share has; every wave is done with the previous tile
+    if (tile + 1 < ntiles) issue_gather(tile + 1, nxt);
     const bool live = tile_fb[tile] >= 0;
     if (live) {
-      // transpose dims 0..511: lane (qd = lane/8, dc = 8*wave + lane%8) reads
-      // 4 token rows of one 16-byte column (lanes 0-7 read 128 contiguous
-      // bytes of a row, lanes 8-15 the row 4 below: disjoint banks) and
-      // writes its 8 dims in a lane-rotated order so that the 8 rows written
-      // together by lanes 0-7 fall in different banks
-      const unsigned char* K = Ks[buf];
-      {
-        const int rot = lane & 7;
-        const int qd = lane >> 3;
-        const int dc = 8 * wave + rot;
-        const uint4 r0 = *reinterpret_cast<const uint4*>(K + (4 * qd + 0) * kKsPitch + dc * 16);
-        const uint4 r1 = *reinterpret_cast<const uint4*>(K + (4 * qd + 1) * kKsPitch + dc * 16);
-        const uint4 r2 = *reinterpret_cast<const uint4*>(K + (4 * qd + 2) * kKsPitch + dc * 16);
-        const uint4 r3 = *reinterpret_cast<const uint4*>(K + (4 * qd + 3) * kKsPitch + dc * 16);
-        const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-        const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-        const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
-        const uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
-        const int pos = quad_pos(qd);
-        // dims (2wi, 2wi+1) of the 4 tokens: low and high halves of word wi
-        uint32_t lo_e[4], hi_e[4], lo_o[4], hi_o[4];
+      // S^T (32 tokens x 16 heads) = KV (32 x 576) . Q^T (576 x 16)
+      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          lo_e[wi] = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-          hi_e[wi] = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-          lo_o[wi] = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-          hi_o[wi] = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int step = 0; step < 8; ++step) {
-          const int e = (step + rot) & 7;  // this lane's dim at this step
-          const int wi = e >> 1;
-          uint32_t lo = lo_e[0], hi = hi_e[0];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (wi == c) {
-              lo = (e & 1) ? lo_o[c] : lo_e[c];
-              hi = (e & 1) ? hi_o[c] : hi_e[c];
-            }
-          }
-          *reinterpret_cast<uint2*>(Vt + (8 * dc + e) * kVtPitch + pos * 2) = make_uint2(lo, hi);
-        }
+      for (int kk = 0; kk < 18; ++kk) {
+        const v8bf a0 = lds_frag(K + l16 * kKsPitch + (4 * kk + g) * 16);
+        const v8bf a1 = lds_frag(K + (16 + l16) * kKsPitch + (4 * kk + g) * 16);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
       }
-    }
-    __syncthreads();
-    if (!live) continue;
-
-    // S^T (32 tokens x 16 heads) = KV (32 x 576) . Q^T (576 x 16)
-    const unsigned char* K = Ks[buf];
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      const v8bf a0 = lds_frag(K + l16 * kKsPitch + (4 * kk + g) * 16);
-      const v8bf a1 = lds_frag(K + (16 + l16) * kKsPitch + (4 * kk + g) * 16);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
-    }
-    // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
-    const uint32_t mask = tile_mask[tile];
-    float z[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      z[r] = s0[r] * scale_log2;
-      z[4 + r] = s1[r] * scale_log2;
-    }
-    if (mask != 0xffffffffu) {  // a tile with skipped tokens (rare)
+      // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
+      const uint32_t mask = tile_mask[tile];
+      float z[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (!((mask >> (4 * g + r)) & 1u)) z[r] = -INFINITY;
-        if (!((mask >> (16 + 4 * g + r)) & 1u)) z[4 + r] = -INFINITY;
+        z[r] = s0[r] * scale_log2;
+        z[4 + r] = s1[r] * scale_log2;
+      }
+      if (mask != 0xffffffffu) {  // a tile with skipped tokens (rare)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (!((mask >> (4 * g + r)) & 1u)) z[r] = -INFINITY;
+          if (!((mask >> (16 + 4 * g + r)) & 1u)) z[4 + r] = -INFINITY;
+        }
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // while the reference is -inf nothing has been accumulated, so the
+      // first finite maximum needs no rescale (alpha stays 1)
+      const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
+      float alpha = 1.f;
+      if (__ballot(raise)) {
+        const float m_new = raise ? tmax : m_ref;
+        if (m_ref != -INFINITY) alpha = exp2f(m_ref - m_new);
+        l_run *= alpha;
+        m_ref = m_new;
+      }
+      if (g == 0) alpha_l[head] = alpha;
+      if (__ballot(alpha != 1.f) && lane == 0) tile_raise[tile] = 1;
+      float p[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        p[r] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+        psum += p[r];
+      }
+      l_run += psum;
+      Pl[wave * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    }
+    lds_barrier();  // P and the rescale factors of all 128 heads are in LDS
+    if (live) {
+      if (tile_raise[tile]) {
+#pragma unroll
+        for (int hb = 0; hb < 8; ++hb) {
+          const float a = alpha_l[16 * hb + l16];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) acc[db][hb] *= a;
+        }
+      }
+      // O^T (64 dims x 128 heads) += V^T (64 x 32) . P^T (32 x 128)
+      v8bf va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) va[db] = v_frag(K, d_base + 16 * db, l16, g);
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) {
+        Frag pb;
+        pb.u = Pl[hb * 64 + lane];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb.v, acc[db][hb], 0, 0, 0);
       }
     }
-    float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
-    if (__ballot(raise)) {
-      const float m_new = raise ? tmax : m_ref;
-      const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
-      if (__ballot(alpha != 1.f && m_ref != -INFINITY)) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-      }
-      l_run *= alpha;
-      m_ref = m_new;
-    }
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p[r] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-      psum += p[r];
-    }
-    l_run += psum;
-    Frag pf;
-    pf.u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7]));
-    // O^T (512 x 16) += V^T (512 x 32) . P^T (32 x 16)
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const v8bf a = lds_frag(Vt + (16 * mt + l16) * kVtPitch + 16 * g);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf.v, acc[mt], 0, 0, 0);
-    }
+  };
+  if (ntiles > 0) issue_gather(0, Ks0);
+  for (int tile = 0; tile < nsteps; tile += 2) {
+    step(tile, Ks0, Ks1);
+    step(tile + 1, Ks1, Ks0);
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-  // lane holds O^T[16mt + 4g + r][head]
-  if (!SPLIT) {
-    uint16_t* o = out + ((int64_t)t * DSA_MLA_HEADS + head) * DSA_MLA_DV + 4 * g;
+  if (g == 0) fin_l[head] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  lds_barrier();
+  // lane holds O^T[d_base + 16db + 4g + r][16hb + l16]
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const v4f x = acc[mt];
-      *reinterpret_cast<uint2*>(o + 16 * mt) =
-          make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
-    }
-    if (lse && g == 0) lse[(int64_t)t * DSA_MLA_HEADS + head] = lse_v;
-  } else {
-    float* o = opart + (((int64_t)t * n_split + split) * DSA_MLA_HEADS + head) * DSA_MLA_DV + 4 * g;
+  for (int hb = 0; hb < 8; ++hb) {
+    const int h = 16 * hb + l16;
+    const float inv = fin_l[h];
+    if (!SPLIT) {
+      uint16_t* o = out + ((int64_t)t * DSA_MLA_HEADS + h) * DSA_MLA_DV + d_base + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const v4f x = acc[mt];
-      *reinterpret_cast<float4*>(o + 16 * mt) =
-          make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+      for (int db = 0; db < 4; ++db) {
+        const v4f x = acc[db][hb];
+        *reinterpret_cast<uint2*>(o + 16 * db) =
+            make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
+      }
+    } else {
+      float* o = opart + (((int64_t)t * n_split + split) * DSA_MLA_HEADS + h) * DSA_MLA_DV + d_base +
+                 4 * g;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const v4f x = acc[db][hb];
+        *reinterpret_cast<float4*>(o + 16 * db) =
+            make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+      }
     }
-    if (g == 0) lpart[((int64_t)t * n_split + split) * DSA_MLA_HEADS + head] = lse_v;
+  }
+  if (g == 0) {
+    if (!SPLIT) {
+      if (lse) lse[(int64_t)t * DSA_MLA_HEADS + head] = lse_v;
+    } else {
+      lpart[((int64_t)t * n_split + split) * DSA_MLA_HEADS + head] = lse_v;
+    }
   }
 }
 
