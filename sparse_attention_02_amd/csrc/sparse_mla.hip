@@ -13,10 +13,11 @@
 // tile of 32 selected tokens:
 //   gather   slots come from a per-split table built once (position -> page
 //            -> slot); the 1152-byte rows go straight from HBM into LDS with
-//            global_load_lds_dwordx4 (row pitch 1184 bytes), double-buffered:
-//            tile i+1 streams in while tile i computes;
-//   S^T      = KV Q^T, wave w taking heads 16w .. 16w+15 (v_mfma_f32_16x16x32_bf16,
-//            its query fragment of 16 heads x 576 dims held in registers);
+//            global_load_lds_dwordx4 (row pitch 1184 bytes) into a ring of
+//            three buffers;
+//   S^T      = KV Q^T, wave w taking heads 16w .. 16w+15 (v_mfma_f32_16x16x32_bf16;
+//            the latent part of its query is held in registers, the rope
+//            part in LDS);
 //   softmax  online, per head, in fp32 by the wave that owns the head; the
 //            reference max is only raised when a score exceeds it by 2^8, so
 //            the accumulator is rarely rescaled (the result does not depend
@@ -28,6 +29,10 @@
 //            token-major tile through transposing LDS reads
 //            (ds_read_b64_tr_b16: four tokens of one dim per lane), in the
 //            token order in which the S^T accumulator holds P.
+// The loop is software-pipelined: step i runs the value product of tile i
+// and the scores of tile i+1 while tile i+2 streams in, with one barrier per
+// step.  Operand reads run ahead of the products that use them (two k-steps
+// in S^T, one head block in O^T), fixed with scheduling fences.
 #include "device_common.h"
 
 namespace dsa {
@@ -46,6 +51,7 @@ constexpr int kMaxChunk = 2048;                // selected tokens per split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleMargin = 8.f;          // log2 units
+constexpr int kQkAhead = 2;                    // S^T k-steps whose operands are in flight
 
 constexpr int kDimsPerWave = DSA_MLA_DV / (kThreads / 64);  // 64
 
@@ -54,6 +60,7 @@ union Frag {
   v8bf v;
 };
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -63,13 +70,9 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 // the S^T accumulator hands out P.  For the 16 lanes of group g, lane L
 // addresses token row 4g + L/4 (and 16 rows below) at dims d0 + 4(L%4).
 __device__ __forceinline__ v8bf v_frag(const unsigned char* K, int d0, int l16, int g) {
-  // the mask keeps the address provably inside the LDS window, which lets
-  // the constant part fold into the instruction offset
-  const uint32_t a =
-      (uint32_t)(uintptr_t)(K + (4 * g + (l16 >> 2)) * kKsPitch + (d0 + 4 * (l16 & 3)) * 2) &
-      0x3ffffu;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(uintptr_t)a);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(uintptr_t)(a + 16 * kKsPitch));
+  const unsigned char* p = K + (4 * g + (l16 >> 2)) * kKsPitch + (d0 + 4 * (l16 & 3)) * 2;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 16 * kKsPitch));
   const v8s x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(v8bf, x);
 }
@@ -100,6 +103,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Per-stage LDS of the tile ring: the gathered tile, the P^T fragments of
+// all 128 heads ([head block][lane]), each head's rescale factor and one
+// flag per wave (some head of the wave was rescaled).  Three stages are
+// separate variables so that the compiler can tell them apart.
+struct Stage {
+  unsigned char* K;
+  uint4* P;
+  float* alpha;
+  uint8_t* raised;
+};
+
 template <bool SPLIT>
 __global__ __launch_bounds__(kThreads)
 void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -107,18 +121,17 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
                        uint16_t* __restrict__ out, float* __restrict__ lse,
                        float* __restrict__ opart, float* __restrict__ lpart, int n_split, int chunk,
                        int n_work, int per_xcd) {
-  // two named buffers rather than one array: the ring alternates between
-  // them at compile time, which lets the compiler see that reading one does
-  // not depend on the loads still streaming into the other
   __shared__ __attribute__((aligned(16))) unsigned char Ks0[kKsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ks1[kKsBytes];
-  __shared__ __attribute__((aligned(16))) uint4 Pl[8 * 64];  // P^T fragments: [head block][lane]
-  __shared__ float alpha_l[DSA_MLA_HEADS];  // rescale factor of each head in this tile
+  __shared__ __attribute__((aligned(16))) unsigned char Ks2[kKsBytes];
+  // P^T, rescale factors and flags of two consecutive tiles (by tile parity)
+  __shared__ __attribute__((aligned(16))) uint4 Pl[2][8 * 64];
+  __shared__ float al[2][DSA_MLA_HEADS];
+  __shared__ __attribute__((aligned(8))) uint8_t rw[2][8];
+  // rope part of the query (dims 512..575) as S^T operands: [k-step][wave][lane]
+  __shared__ __attribute__((aligned(16))) uint4 Qr[2][8 * 64];
   __shared__ float fin_l[DSA_MLA_HEADS];    // 1 / softmax denominator of each head
   __shared__ int32_t slots[kMaxChunk];
-  __shared__ int32_t tile_fb[kMaxChunk / kMlaTile];    // a valid slot of the tile, -1 if none
-  __shared__ uint32_t tile_mask[kMaxChunk / kMlaTile];  // bit x: token x of the tile is valid
-  __shared__ int32_t tile_raise[kMaxChunk / kMlaTile];   // some head rescaled in the tile
 
   // consecutive work items land on the same XCD (work-groups are dealt to
   // the 8 XCDs round-robin), so the splits and the MTP rows of a request
@@ -132,7 +145,6 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int j0 = split * chunk;
   const int ntok = max(0, min(k, j0 + chunk) - j0);
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
-  const int nsteps = (ntiles + 1) & ~1;  // even: a padding tile has no valid token
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,7 +154,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int head = wave * 16 + l16;
 
   // position -> slot for the whole split (-1: skipped)
-  for (int i = tid; i < nsteps * kMlaTile; i += kThreads) {
+  for (int i = tid; i < ntiles * kMlaTile; i += kThreads) {
     int slot = -1;
     if (i < ntok) {
       const int s = idx[(int64_t)t * k + j0 + i];
@@ -154,49 +166,59 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     slots[i] = slot;
   }
   __syncthreads();
-  for (int tt = tid; tt < nsteps; tt += kThreads) {
-    int fb = -1;
-    uint32_t mask = 0;
-    for (int x = 0; x < kMlaTile; ++x) {
-      const int sl = slots[tt * kMlaTile + x];
-      if (sl >= 0) {
-        mask |= 1u << x;
-        if (fb < 0) fb = sl;
-      }
-    }
-    tile_fb[tt] = fb;
-    tile_mask[tt] = mask;
-    tile_raise[tt] = 0;
-  }
-  __syncthreads();
 
-  // B operand of S^T: q[t, head, 32kk + 8g .. +8]
-  v8bf qf[18];
+  // B operand of S^T: q[t, head, 32kk + 8g .. +8]; the latent part in
+  // registers, the rope part (k-steps 16 and 17) in LDS
+  v8bf qf[16];
   {
     const uint4* src =
         reinterpret_cast<const uint4*>(q + ((int64_t)t * DSA_MLA_HEADS + head) * DSA_MLA_DIM) + g;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
+    for (int kk = 0; kk < 16; ++kk) {
       Frag f;
       f.u = src[4 * kk];
       qf[kk] = f.v;
     }
+    Qr[0][wave * 64 + lane] = src[4 * 16];
+    Qr[1][wave * 64 + lane] = src[4 * 17];
   }
 
+  // slots of a tile, one per lane: lane L holds token L % 32 (-1: skipped or
+  // past the split)
+  auto slot_vec = [&](int tile) -> int {
+    return tile < ntiles ? slots[tile * kMlaTile + (lane & 31)] : -1;
+  };
+  // bit x: token x of the tile has a row
+  auto tile_bits = [&](int sv) -> uint32_t { return (uint32_t)__ballot(sv >= 0); };
+
   // one tile: 37 wave-wide loads of 64 x 16 bytes; lane L of load n fills
-  // byte 16*(64n + L) of the buffer = token (64n+L)/73, chunk (64n+L)%73
-  auto issue_gather = [&](int tile, unsigned char* dst) {
-    const int fb = tile_fb[tile];
-    if (fb < 0) return;
-    for (int n = wave; n < kKsLoads; n += kThreads / 64) {
-      const int c = 64 * n + lane;
-      const int tok = c / kKsChunks;
-      int cc = c - tok * kKsChunks;
-      int slot = tok < kMlaTile ? slots[tile * kMlaTile + tok] : -1;
-      if (slot < 0) slot = fb;  // padding lanes and skipped tokens re-read a valid row
-      if (cc >= 72) cc = 0;  // pad chunks
-      const uint16_t* src = kv + (int64_t)slot * DSA_MLA_DIM + cc * 8;
-      __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+  // byte 16*(64n + L) of the buffer = token (64n+L)/74, chunk (64n+L)%74.
+  // The 64 lanes of a load span at most two tokens, whose slots come from
+  // the tile's slot vector by lane reads (no LDS round trip per load).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_gather = [&](int sv, uint32_t bits, unsigned char* dst) {
+    if (bits == 0) return;
+    const int fb = __builtin_amdgcn_readlane(sv, __builtin_ctz(bits));
+    // recomputed on every call: keeping the per-load offsets live across
+    // the tile loop would cost registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < (kKsLoads + 7) / 8; ++i) {
+      const int n = wave_u + 8 * i;
+      if (n < kKsLoads) {
+        const int ta = (64 * n) / kKsChunks;  // first token of the load
+        const int sa = __builtin_amdgcn_readlane(sv, ta);
+        const int sb = __builtin_amdgcn_readlane(sv, min(ta + 1, kMlaTile - 1));
+        const int c = 64 * n + ln;
+        const int tok = c / kKsChunks;
+        int cc = c - tok * kKsChunks;
+        int slot = tok == ta ? sa : sb;
+        if (slot < 0) slot = fb;  // skipped tokens re-read a valid row
+        if (cc >= 72) cc = 0;     // pad chunks
+        const uint16_t* src = kv + (int64_t)slot * DSA_MLA_DIM + cc * 8;
+        __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+      }
     }
   };
 
@@ -210,92 +232,144 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   float l_run = 0.f;
   const int d_base = kDimsPerWave * wave;
 
-  // one tile: K holds it, nxt receives the next one meanwhile
-  auto step = [&](int tile, const unsigned char* K, unsigned char* nxt) {
-    wait_vm_all();  // this wave's share of the tile has landed in LDS
-    lds_barrier();  // every share has; every wave is done with the previous tile
-    if (tile + 1 < ntiles) issue_gather(tile + 1, nxt);
-    const bool live = tile_fb[tile] >= 0;
-    if (live) {
-      // S^T (32 tokens x 16 heads) = KV (32 x 576) . Q^T (576 x 16)
-      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  // S^T of a tile and its online softmax; P^T and the rescale factors go to
+  // the tile's stage.  Straight-line code, so that the value product of the
+  // previous tile can be scheduled into it.
+  auto qk_softmax = [&](uint32_t mask, const Stage& st) {
+    // S^T (32 tokens x 16 heads) = KV (32 x 576) . Q^T (576 x 16)
+    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // the operands of k-step kk + kQkAhead are read while kk's products run;
+    // the scheduling fences keep the compiler from regrouping them
+    const unsigned char* kr = st.K + l16 * kKsPitch + g * 16;
+    v8bf a0[kQkAhead + 1], a1[kQkAhead + 1];
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        const v8bf a0 = lds_frag(K + l16 * kKsPitch + (4 * kk + g) * 16);
-        const v8bf a1 = lds_frag(K + (16 + l16) * kKsPitch + (4 * kk + g) * 16);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
-      }
-      // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
-      const uint32_t mask = tile_mask[tile];
-      float z[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        z[r] = s0[r] * scale_log2;
-        z[4 + r] = s1[r] * scale_log2;
-      }
-      if (mask != 0xffffffffu) {  // a tile with skipped tokens (rare)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (!((mask >> (4 * g + r)) & 1u)) z[r] = -INFINITY;
-          if (!((mask >> (16 + 4 * g + r)) & 1u)) z[4 + r] = -INFINITY;
-        }
-      }
-      float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      // while the reference is -inf nothing has been accumulated, so the
-      // first finite maximum needs no rescale (alpha stays 1)
-      const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
-      float alpha = 1.f;
-      if (__ballot(raise)) {
-        const float m_new = raise ? tmax : m_ref;
-        if (m_ref != -INFINITY) alpha = exp2f(m_ref - m_new);
-        l_run *= alpha;
-        m_ref = m_new;
-      }
-      if (g == 0) alpha_l[head] = alpha;
-      if (__ballot(alpha != 1.f) && lane == 0) tile_raise[tile] = 1;
-      float p[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p[r] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-        psum += p[r];
-      }
-      l_run += psum;
-      Pl[wave * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    for (int d = 0; d < kQkAhead; ++d) {
+      a0[d] = lds_frag(kr + 64 * d);
+      a1[d] = lds_frag(kr + 16 * kKsPitch + 64 * d);
     }
-    lds_barrier();  // P and the rescale factors of all 128 heads are in LDS
-    if (live) {
-      if (tile_raise[tile]) {
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      if (kk + kQkAhead < 18) {
+        a0[(kk + kQkAhead) % (kQkAhead + 1)] = lds_frag(kr + 64 * (kk + kQkAhead));
+        a1[(kk + kQkAhead) % (kQkAhead + 1)] = lds_frag(kr + 16 * kKsPitch + 64 * (kk + kQkAhead));
+      }
+      Frag qb;
+      if (kk < 16) qb.v = qf[kk < 16 ? kk : 0];  // (the index guard only silences the unrolled tail)
+      else qb.u = Qr[kk - 16][wave * 64 + lane];
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[kk % (kQkAhead + 1)], qb.v, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[kk % (kQkAhead + 1)], qb.v, s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
+    float z[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      z[r] = (mask >> (4 * g + r)) & 1u ? s0[r] * scale_log2 : -INFINITY;
+      z[4 + r] = (mask >> (16 + 4 * g + r)) & 1u ? s1[r] * scale_log2 : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    {  // max over the four 16-lane rows (lanes l, l^16, l^32, l^48), in VALU
+      const v2u x = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                     false, false);
+      tmax = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+      const v2u y = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                     false, false);
+      tmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+    }
+    // while the reference is -inf nothing has been accumulated, so the
+    // first finite maximum needs no rescale (alpha stays 1)
+    const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
+    const float m_new = raise ? tmax : m_ref;
+    const float alpha = m_ref == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_run *= alpha;
+    m_ref = m_new;
+    st.alpha[head] = alpha;  // the four lanes of a head store the same value
+    st.raised[wave] = __ballot(alpha != 1.f) != 0;
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      p[r] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+      psum += p[r];
+    }
+    l_run += psum;
+    st.P[wave * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+  };
+
+  // O^T (64 dims x 128 heads) += V^T (64 x 32) . P^T (32 x 128) for a tile
+  // whose P^T is in its stage
+  auto pv = [&](const Stage& st) {
+    v8bf va[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) va[db] = v_frag(st.K, d_base + 16 * db, l16, g);
+    // P^T of head block hb + 1 is read while hb's products run
+    Frag pb[2];
+    pb[0].u = st.P[lane];
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      if (hb + 1 < 8) pb[(hb + 1) & 1].u = st.P[(hb + 1) * 64 + lane];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[hb & 1].v, acc[db][hb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Step `tile`: the value product of `tile` and the scores of `tile + 1`,
+  // while `tile + 2` streams into the third stage.
+  // Step `tile`: the value product of `tile` and the scores of `tile + 1`,
+  // while `tile + 2` streams into the third stage.  Carried between steps:
+  // the token masks of `tile` and `tile + 1`, the slot vector of `tile + 2`.
+  uint32_t bits_c = 0, bits_n1 = 0, bits_n2 = 0;
+  int sv_n2 = -1;
+  auto step = [&](int tile, const Stage& cur, const Stage& nx1, const Stage& nx2) {
+    wait_vm_all();  // this wave's share of tile + 1 has landed
+    lds_barrier();  // every share has; P^T of `tile` is complete; the third stage is free
+    issue_gather(sv_n2, bits_n2, nx2.K);
+    const int sv_n3 = slot_vec(tile + 3);
+    const uint64_t rescaled = *reinterpret_cast<const uint64_t*>(cur.raised);
+    if (bits_n1) qk_softmax(bits_n1, nx1);
+    if (bits_c) {
+      if (rescaled) {
 #pragma unroll
         for (int hb = 0; hb < 8; ++hb) {
-          const float a = alpha_l[16 * hb + l16];
+          const float a = cur.alpha[16 * hb + l16];
 #pragma unroll
           for (int db = 0; db < 4; ++db) acc[db][hb] *= a;
         }
       }
-      // O^T (64 dims x 128 heads) += V^T (64 x 32) . P^T (32 x 128)
-      v8bf va[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) va[db] = v_frag(K, d_base + 16 * db, l16, g);
-#pragma unroll
-      for (int hb = 0; hb < 8; ++hb) {
-        Frag pb;
-        pb.u = Pl[hb * 64 + lane];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb.v, acc[db][hb], 0, 0, 0);
-      }
+      pv(cur);
     }
+    bits_c = bits_n1;
+    bits_n1 = bits_n2;
+    bits_n2 = tile_bits(sv_n3);
+    sv_n2 = sv_n3;
   };
-  if (ntiles > 0) issue_gather(0, Ks0);
-  for (int tile = 0; tile < nsteps; tile += 2) {
-    step(tile, Ks0, Ks1);
-    step(tile + 1, Ks1, Ks0);
+
+  // stages of tiles 3i, 3i+1, 3i+2; P^T and the rescale data alternate by
+  // tile parity
+  auto stage = [&](unsigned char* K, int tile) {
+    const int par = tile & 1;
+    return Stage{K, Pl[par], al[par], rw[par]};
+  };
+  {
+    const int sv0 = slot_vec(0), sv1 = slot_vec(1);
+    sv_n2 = slot_vec(2);
+    bits_c = tile_bits(sv0);
+    bits_n1 = tile_bits(sv1);
+    bits_n2 = tile_bits(sv_n2);
+    issue_gather(sv0, bits_c, Ks0);
+    wait_vm_all();
+    lds_barrier();
+    issue_gather(sv1, bits_n1, Ks1);
+    if (bits_c) qk_softmax(bits_c, stage(Ks0, 0));
+  }
+  for (int tile = 0; tile < ntiles; tile += 3) {
+    step(tile, stage(Ks0, tile), stage(Ks1, tile + 1), stage(Ks2, tile + 2));
+    step(tile + 1, stage(Ks1, tile + 1), stage(Ks2, tile + 2), stage(Ks0, tile + 3));
+    step(tile + 2, stage(Ks2, tile + 2), stage(Ks0, tile + 3), stage(Ks1, tile + 4));
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
