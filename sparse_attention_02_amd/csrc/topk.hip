@@ -7,13 +7,14 @@
 //   1. hist1   per-row histogram of the top 11 key bits (LDS histograms added
 //              into global memory).  The fused decode step builds it inside
 //              the indexer scan instead (no extra pass over the scores).
-//   2. thresh  (row): the bin b1 holding the K-th largest key.
-//   3. collect (row x 8192-score segment): keys in bins above b1 are
-//              selected outright, keys in b1 become candidates; one atomic
-//              per work-group reserves the output ranges, ranks inside the
-//              work-group come from a block scan.  It also histograms bits
-//              20..10 of the candidates (hist2).
-//   4. final   (row): the second digit from hist2, the third from one pass
+//   2. collect (row x 8192-score segment): each work-group finds the bin b1
+//              holding the K-th largest key from hist1 (while its score loads
+//              are in flight); keys in bins above b1 are selected outright,
+//              keys in b1 become candidates; one atomic per work-group
+//              reserves the output ranges, ranks inside the work-group come
+//              from a block scan.  It also histograms bits 20..10 of the
+//              candidates (hist2).
+//   3. final   (row): the second digit from hist2, the third from one pass
 //              over the candidates, ties at the exact threshold resolved by
 //              a radix select on the position (lowest positions win), then
 //              the K positions are written in ascending order (LDS bitmap,
@@ -134,47 +135,56 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* ws
   return before + inc - x;
 }
 
-__global__ __launch_bounds__(kHistThreads) void topk_thresh_kernel(BatchArgs b, int k,
-                                                                    const uint32_t* __restrict__ hist,
-                                                                    int32_t* __restrict__ ctrl) {
-  __shared__ uint32_t h[kTopkBins];
-  __shared__ uint32_t scan[kHistThreads];
+__global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
+    BatchArgs b, const float* __restrict__ scores, int64_t ld, int k,
+    const uint32_t* __restrict__ hist1, int32_t* __restrict__ ctrl, int32_t* __restrict__ idx,
+    uint2* __restrict__ cand, int64_t cand_stride, uint32_t* __restrict__ hist2) {
+  __shared__ uint32_t h1[kTopkBins];
+  __shared__ uint32_t h2[kTopkBins];
+  __shared__ uint32_t scan[kCollectThreads];
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t s_base[2];
   __shared__ int s_bin;
   __shared__ uint32_t s_above;
   const int t = blockIdx.x;
   const int v = row_len(b, t);
-  if (v <= k) {
-    if (threadIdx.x == 0) ctrl[t * kCtrlWords + kCtrlB1] = -1;
-    return;
-  }
-  for (int i = threadIdx.x; i < kTopkBins; i += kHistThreads) h[i] = hist[(int64_t)t * kTopkBins + i];
-  __syncthreads();
-  find_cut(h, kTopkBins, (uint32_t)k, &s_bin, &s_above, scan);
-  if (threadIdx.x == 0) ctrl[t * kCtrlWords + kCtrlB1] = s_bin;
-}
-
-__global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
-    BatchArgs b, const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ ctrl,
-    int32_t* __restrict__ idx, uint2* __restrict__ cand, int64_t cand_stride,
-    uint32_t* __restrict__ hist2) {
-  __shared__ uint32_t h2[kTopkBins];
-  __shared__ uint32_t wsum[16];
-  __shared__ uint32_t s_base[2];
-  const int t = blockIdx.x;
-  const int v = row_len(b, t);
   const int s0 = blockIdx.y * kTopkSeg;
   if (s0 >= v) return;
-  const int b1 = ctrl[t * kCtrlWords + kCtrlB1];
   const float* row = scores + (int64_t)t * ld;
-  for (int i = threadIdx.x; i < kTopkBins; i += kCollectThreads) h2[i] = 0u;
+  const bool all = v <= k;  // every visible position is selected
 
-  // element j of this thread is position s0 + tid + 256 j (coalesced
-  // loads, all issued before any is used: positions past the row re-read
-  // its last score and are masked below)
+  // the row's first-digit histogram, then the segment's scores: element j
+  // of this thread is position s0 + tid + 256 j (coalesced loads, all
+  // issued before any is used: positions past the row re-read its last
+  // score and are masked below).  The threshold search below runs while
+  // the score loads are in flight.
+  constexpr int kHistPer = kTopkBins / kCollectThreads;
+  uint32_t hv[kHistPer];
+#pragma unroll
+  for (int i = 0; i < kHistPer; ++i)
+    hv[i] = all ? 0u : hist1[(int64_t)t * kTopkBins + threadIdx.x + i * kCollectThreads];
   uint32_t key[kPerThread];
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j)
     key[j] = float_key(row[min(s0 + (int)threadIdx.x + j * kCollectThreads, v - 1)]);
+#pragma unroll
+  for (int i = 0; i < kHistPer; ++i) {
+    h1[threadIdx.x + i * kCollectThreads] = hv[i];
+    h2[threadIdx.x + i * kCollectThreads] = 0u;
+  }
+  __syncthreads();
+  // b1: the first-digit bin holding the K-th largest key (-1: all selected);
+  // every segment of the row finds the same bin, the first records it
+  int b1 = -1;
+  if (!all) {
+    // (a histogram holding fewer than k keys -- scores never written for a
+    // page with an invalid id -- leaves the bin at -1; the writes below stay
+    // inside the row's k slots either way)
+    if (threadIdx.x == 0) s_bin = -1;
+    find_cut(h1, kTopkBins, (uint32_t)k, &s_bin, &s_above, scan);
+    b1 = s_bin;
+  }
+  if (blockIdx.y == 0 && threadIdx.x == 0) ctrl[t * kCtrlWords + kCtrlB1] = b1;
   uint32_t am = 0, em = 0;  // bit j: element j is above / a candidate
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
@@ -185,7 +195,6 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
       else if (d == b1) em |= 1u << j;
     }
   }
-  __syncthreads();  // h2 zeroed
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j)
     if (em & (1u << j)) atomicAdd(&h2[(key[j] >> 10) & (kTopkBins - 1)], 1u);
@@ -198,13 +207,17 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
     s_base[1] = tot_e ? atomicAdd(&ctrl[t * kCtrlWords + kCtrlCand], (int)tot_e) : 0;
   }
   __syncthreads();
-  int32_t* out = idx + (int64_t)t * k + s_base[0] + ex_a;
+  int32_t* out = idx + (int64_t)t * k;
+  const uint32_t ra = s_base[0] + ex_a;  // rank of this thread's first "above" position
   uint2* cl = cand + (int64_t)t * cand_stride + s_base[1] + ex_e;
   int na = 0, ne = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int s = s0 + threadIdx.x + j * kCollectThreads;
-    if (am & (1u << j)) out[na++] = s;
+    if (am & (1u << j)) {
+      if (ra + na < (uint32_t)k) out[ra + na] = s;
+      ++na;
+    }
     if (em & (1u << j)) cl[ne++] = make_uint2(key[j], (uint32_t)s);
   }
   if (b1 >= 0) {
@@ -445,9 +458,8 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
   uint2* cand = reinterpret_cast<uint2*>(base + L.cand_off);
   const int segs = std::max(1, (b.max_seqlen_k + kTopkSeg - 1) / kTopkSeg);
   dim3 g2(b.T, segs);
-  hipLaunchKernelGGL(topk_thresh_kernel, dim3(b.T), dim3(kHistThreads), 0, s, b, k, hist1, ctrl);
-  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k, ctrl,
-                     idx, cand, (int64_t)b.max_seqlen_k, hist2);
+  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k, hist1,
+                     ctrl, idx, cand, (int64_t)b.max_seqlen_k, hist2);
   hipLaunchKernelGGL(topk_final_kernel, dim3(b.T), dim3(kFinalThreads), 0, s, b, k, ctrl, hist2,
                      idx, cand, (int64_t)b.max_seqlen_k);
   return hipGetLastError();
