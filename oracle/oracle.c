@@ -18,6 +18,10 @@
  *    L - n + 1 + i tokens (3 rows at L = 10 see 8, 9, 10).
  *  - "[SGLang] NSA", NSAMetadata: page tables map a request's token
  *    positions to physical pages of 64 tokens.
+ *  - "MTP and sparse attention: NSA and DSA", new demands on inference
+ *    engines, and "[SGLang] NSA", forward_decode: the step's new tokens are
+ *    written into the paged latent cache and, FP8-quantised with a per-key
+ *    scale, into the indexer-key cache (oracle_cache_append).
  * Ties in the selection go to the lower position.  FP8 values are OCP
  * e4m3fn (the pages say FP8 / E4M3 only; e4m3fn is the reading taken).
  */
@@ -366,4 +370,70 @@ void oracle_dense_mla(const oracle_batch* bt, int32_t H, int32_t D, int32_t Dv, 
                       double* out, double* lse, int threads) {
   mla_ctx c = {bt, H, D, Dv, q, kv, NULL, 0, sm_scale, rows, out, lse};
   run_items((int64_t)n_rows * H, threads, mla_item, &c);
+}
+
+/* ---- cache append ---------------------------------------------------------
+ * "MTP and sparse attention: NSA and DSA", new demands on inference engines:
+ * the indexer keys are a second paged cache beside the latent, stored as
+ * FP8 with a 4-byte scale per key (cache accounting listing: 128 + 4 bytes
+ * per token).  "[SGLang] NSA", forward_decode: the new tokens' latent rows
+ * go into the paged pool before the attention.  Readings taken where the
+ * pages stop: one scale per key = its largest magnitude / 448 in fp32 (1 for
+ * an all-zero key), codes = e4m3fn(k / scale) rounded to nearest with ties
+ * to the even code and saturated at +-448; the quotient is formed in fp32
+ * (the precision the stored scale has); row j of a request with n rows and L
+ * cached tokens is the token at position L - n + j. */
+
+/* OCP e4m3fn code of x: the nearest of the 127 finite magnitudes (codes
+ * 0x00 .. 0x7E, found by trying each), ties to the even code, which is the
+ * even mantissa; magnitudes beyond 448 take 448; the sign is kept (-0.0 ->
+ * 0x80). */
+uint8_t oracle_e4m3_encode(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(sign | 0x7F);
+  if (isinf(x)) return (uint8_t)(sign | 0x7E);
+  const double a = fabs((double)x);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 0x7F; ++c) {
+    const double d = fabs(a - oracle_e4m3_decode((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* Writes the n_rows new tokens into the caches: k_new bf16 [T, D_idx],
+ * kv_new bf16 [T, D_kv]; k8 [num_pages * page_size, D_idx], ks [...],
+ * kv [..., D_kv].  Rows whose page id lies outside [0, num_pages), or whose
+ * position is negative, write nothing. */
+void oracle_cache_append(const oracle_batch* bt, int32_t num_pages, int32_t D_idx, int32_t D_kv,
+                         const uint16_t* k_new, const uint16_t* kv_new, uint8_t* k8, float* ks,
+                         uint16_t* kv) {
+  for (int32_t b = 0; b < bt->B; ++b) {
+    const int64_t n = bt->cu_q[b + 1] - bt->cu_q[b];
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t t = bt->cu_q[b] + j;
+      const int64_t pos = (int64_t)bt->seqlens_k[b] - n + j;
+      if (pos < 0 || pos >= (int64_t)bt->max_pages * bt->page_size) continue;
+      const int64_t page = bt->page_table[(int64_t)b * bt->max_pages + pos / bt->page_size];
+      if (page < 0 || page >= num_pages) continue;
+      const int64_t slot = page * bt->page_size + pos % bt->page_size;
+      float amax = 0.0f;
+      for (int d = 0; d < D_idx; ++d) {
+        const float x = (float)oracle_bf16_decode(k_new[t * D_idx + d]);
+        if (fabsf(x) > amax) amax = fabsf(x);
+      }
+      const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+      for (int d = 0; d < D_idx; ++d) {
+        const float x = (float)oracle_bf16_decode(k_new[t * D_idx + d]);
+        const float qv = x / scale;
+        k8[slot * D_idx + d] = oracle_e4m3_encode(qv);
+      }
+      ks[slot] = scale;
+      for (int d = 0; d < D_kv; ++d) kv[slot * D_kv + d] = kv_new[t * D_kv + d];
+    }
+  }
 }

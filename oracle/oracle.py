@@ -61,6 +61,9 @@ def lib():
         L.oracle_topk_rows.argtypes = [vp, i64, vp, i32, i32, dbl, vp, vp, i64, vp, vp, ci]
         L.oracle_sparse_mla.argtypes = [bp, i32, i32, i32, vp, vp, vp, i32, dbl, vp, i32, vp, vp, ci]
         L.oracle_dense_mla.argtypes = [bp, i32, i32, i32, vp, vp, dbl, vp, i32, vp, vp, ci]
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_cache_append.argtypes = [bp, i32, i32, i32, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -98,6 +101,25 @@ def e4m3_decode(code: int) -> float:
 
 def bf16_decode(bits: int) -> float:
     return float(lib().oracle_bf16_decode(int(bits)))
+
+
+def e4m3_encode(x: float) -> int:
+    """OCP e4m3fn code of the float32 value x (nearest, ties to even, saturating)."""
+    return int(lib().oracle_e4m3_encode(float(x)))
+
+
+def cache_append(meta: Meta, num_pages: int, k_new, kv_new, k8, k_scale, kv):
+    """Writes the batch's new tokens into copies of the caches and returns them:
+    k_new uint16 (bf16) [T, 128], kv_new uint16 [T, 576]; k8 uint8 [pages, 64, 128],
+    k_scale float32 [pages, 64], kv uint16 [pages, 64, 576]."""
+    k_new = np.ascontiguousarray(k_new, np.uint16)
+    kv_new = np.ascontiguousarray(kv_new, np.uint16)
+    k8 = np.array(k8, np.uint8, copy=True, order="C")
+    k_scale = np.array(k_scale, np.float32, copy=True, order="C")
+    kv = np.array(kv, np.uint16, copy=True, order="C")
+    lib().oracle_cache_append(meta.ref(), int(num_pages), k_new.shape[-1], kv_new.shape[-1],
+                              _p(k_new), _p(kv_new), _p(k8), _p(k_scale), _p(kv))
+    return k8, k_scale, kv
 
 
 def index_score(meta: Meta, q8, q_scale, w, k8, k_scale, rows, ld=None, threads=0):

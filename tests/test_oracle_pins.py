@@ -58,6 +58,90 @@ def test_synth_e4m3_encoder_matches_torch_rounding():
     assert synth.e4m3_encode(1000.0) == 0x7E  # saturates
 
 
+def test_oracle_e4m3_encode_inverts_decode_on_every_code():
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert O.e4m3_encode(O.e4m3_decode(c)) == c, hex(c)
+
+
+def test_oracle_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.normal(0, 60, 3000), rng.normal(0, 0.01, 1000),
+                        rng.uniform(-448, 448, 1000), rng.normal(0, 2.0 ** -8, 500)])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.e4m3_encode(float(v)) for v in x], np.uint8)
+    assert np.array_equal(ref, got)
+
+
+def test_oracle_e4m3_encode_ties_to_even_and_saturates():
+    # midpoints between neighbouring codes go to the even code (even mantissa)
+    for c in range(0, 0x7E):
+        lo, hi = O.e4m3_decode(c), O.e4m3_decode(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2  # exact in float32
+        assert O.e4m3_encode(float(mid)) == (c if c % 2 == 0 else c + 1)
+        assert O.e4m3_encode(-float(mid)) == 0x80 | (c if c % 2 == 0 else c + 1)
+    assert O.e4m3_encode(2.0 ** -10) == 0x00  # half the smallest subnormal: tie to 0
+    assert O.e4m3_encode(448.0) == 0x7E
+    assert O.e4m3_encode(460.0) == 0x7E
+    assert O.e4m3_encode(1e30) == 0x7E and O.e4m3_encode(-1e30) == 0xFE
+    assert O.e4m3_encode(-0.0) == 0x80 and O.e4m3_encode(0.0) == 0x00
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+def test_cache_append_places_quantises_and_leaves_other_slots():
+    # three requests of 1, 2 and 3 new rows; the third mirrors the worked
+    # example of "[SGLang] NSA" (3 rows onto kv_len 10: they are positions 7,
+    # 8, 9); the second request's last page id is outside the pool
+    rng = np.random.default_rng(5)
+    P, num_pages = 64, 12
+    L = np.array([70, 129, 10], np.int32)
+    n = np.array([1, 2, 3])
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    T = int(cu[-1])
+    pt = np.full((3, 3), -1, np.int32)
+    pt[0, :2] = [7, 2]
+    pt[1, :3] = [5, 9, num_pages + 4]
+    pt[2, :1] = [3]
+    meta = O.Meta(cu, L, pt)
+    k_new = _bf16_bits(rng.normal(0, 1, (T, 128)) * rng.uniform(0.01, 100, (T, 1)))
+    k_new[5] = 0  # an all-zero key
+    kv_new = rng.integers(0, 1 << 16, (T, 576)).astype(np.uint16)
+    k8 = np.full((num_pages, P, 128), 0xA5, np.uint8)
+    ks = np.full((num_pages, P), -7.0, np.float32)
+    kv = np.full((num_pages, P, 576), 0x1234, np.uint16)
+    k8o, kso, kvo = O.cache_append(meta, num_pages, k_new, kv_new, k8, ks, kv)
+    expect = {0: (2, 5), 3: (3, 7), 4: (3, 8), 5: (3, 9)}  # row -> (page, slot in page)
+    # row 1 (request 1, position 127) lies on page 9; row 2 (position 128) on
+    # the page outside the pool, which is not written
+    expect[1] = (9, 63)
+    touched = np.zeros((num_pages, P), bool)
+    for t, (pg, s) in expect.items():
+        touched[pg, s] = True
+        x = torch.from_numpy(k_new[t].view(np.int16)).view(torch.bfloat16).float().numpy()
+        amax = np.float32(np.abs(x).max())
+        scale = np.float32(amax / np.float32(448)) if amax > 0 else np.float32(1)
+        assert kso[pg, s] == scale
+        qv = (x / scale).astype(np.float32)
+        ref = torch.from_numpy(qv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(k8o[pg, s], ref)
+        if amax > 0:
+            assert np.abs(O.e4m3_decode(int(k8o[pg, s][np.argmax(np.abs(x))]))) == 448.0
+            deq = np.array([O.e4m3_decode(int(c)) for c in k8o[pg, s]]) * float(scale)
+            assert np.all(np.abs(deq - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * float(scale))
+        else:
+            assert scale == 1 and not k8o[pg, s].any()
+        assert np.array_equal(kvo[pg, s], kv_new[t])
+    assert np.all(k8o[~touched] == 0xA5) and np.all(kso[~touched] == -7.0)
+    assert np.all(kvo[~touched] == 0x1234)
+
+
 # ------------------------------------------------------------- visibility
 
 def test_visibility_worked_example():
