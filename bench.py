@@ -259,6 +259,57 @@ def prefill_measure(steps):
     return res
 
 
+# bytes one appended token moves: its bf16 key (256) and latent row (1152)
+# read; its FP8 key (128), scale (4) and latent row (1152) written
+APPEND_BYTES_PER_TOKEN = 2 * 128 + 2 * 576 + 128 + 4 + 2 * 576
+
+
+def append_measure(iters=200):
+    """dsa_cache_append on the decode batch's shape (64 requests x 2 rows
+    onto 131072 cached tokens) and on a 4096-row prefill chunk; the page
+    pool holds the pages the new rows land on."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    res = {}
+    rng = np.random.default_rng(0)
+    for name, B, n, L in (("decode-b64-mtp1-ctx131072", 64, 2, 131072),
+                          ("prefill-4096-on-61440", 1, 4096, 65536)):
+        maxp = L // 64
+        need = B * ((n + 63) // 64 + 1)
+        pool = rng.permutation(need).astype(np.int32)
+        pt = np.full((B, maxp), -1, np.int32)
+        per = need // B
+        for b in range(B):
+            first = (L - n) // 64
+            pt[b, first:first + per] = pool[b * per:(b + 1) * per][:maxp - first]
+        cu = np.arange(0, B * n + 1, n, dtype=np.int32)
+        dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+        batch = dsa.Batch(dev(cu), dev(np.full(B, L, np.int32)), dev(pt), need, n, L)
+        T = B * n
+        k_new = torch.randn((T, 128), device="cuda").to(torch.bfloat16)
+        kv_new = torch.randn((T, 576), device="cuda").to(torch.bfloat16)
+        k8 = torch.zeros((need, 64, 128), dtype=torch.uint8, device="cuda")
+        ks = torch.zeros((need, 64), dtype=torch.float32, device="cuda")
+        kv = torch.zeros((need, 64, 576), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: dsa.dsa_cache_append(batch, k_new, kv_new, k8, ks, kv)  # noqa: E731
+        # a single call is shorter than the host's launch cost, so the calls
+        # are captured in a graph and replayed (device time per call)
+        fn()
+        torch.cuda.synchronize()
+        reps = 50
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        ms = wall_ms(g.replay, max(2, iters // reps), warmup=2) / reps
+        res[name] = {"tokens": T, "us_per_call": ms * 1e3,
+                     "algorithmic_bytes": T * APPEND_BYTES_PER_TOKEN,
+                     "gbs": T * APPEND_BYTES_PER_TOKEN / (ms * 1e-3) / 1e9}
+    return res
+
+
 def mli_measure(steps):
     """Two-stream MLI step vs the same kernels back to back on one stream."""
     import numpy as np
@@ -371,6 +422,8 @@ def main():
         log(f"prefill {result['prefill']}")
         result["mli"] = mli_measure(max(5, args.steps // 2))
         log(f"mli {result['mli']}")
+        result["cache_append"] = append_measure()
+        log(f"cache append {result['cache_append']}")
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         rows = list(range(min(args.cpu_rows, T)))

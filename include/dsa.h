@@ -105,6 +105,31 @@ int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_
                     const float* w, const uint8_t* k8_cache, const float* k_scale, float* scores,
                     int64_t ld, void* stream);
 
+/* Cache append: the step's new tokens into the two paged caches
+ * ("MTP and sparse attention: NSA and DSA", new demands on inference
+ * engines: the indexer keys form a second paged cache beside the latent, and
+ * the cache accounting listing gives 128 FP8 bytes plus a 4-byte scale per
+ * key; "[SGLang] NSA", forward_decode: the new tokens' latent rows are stored
+ * into the paged pool before the attention runs).
+ * Query row j of request b (n_b rows, L_b cached tokens including them) is
+ * the token at position p = L_b - n_b + j; its slot is
+ * page_table[b][p / 64] * 64 + p % 64.
+ *  k_new    bf16 [T, 128]  the rows' indexer keys (finite values)
+ *  kv_new   bf16 [T, 576]  the rows' latent (512) + rope (64) values
+ *  k8_cache uint8 [num_pages, 64, 128] out: k8[slot, d] = e4m3fn(k_new[t, d] / s)
+ *           rounded to nearest even, where s = max_d |k_new[t, d]| / 448 in
+ *           fp32 (s = 1 for an all-zero key); the key's largest magnitude
+ *           maps to +-448
+ *  k_scale  f32 [num_pages, 64] out: k_scale[slot] = s
+ *  kv_cache bf16 [num_pages, 64, 576] out: kv_cache[slot] = kv_new[t] (bit copy)
+ * Slots of rows whose page id is outside [0, num_pages), or whose position
+ * is negative, are not written; no other slot is touched.  kv_new and
+ * kv_cache must be 16-byte aligned, k_new and k_scale 4-byte, k8_cache
+ * 2-byte.
+ * Errors: INVALID_ARG (null pointers with T > 0, misalignment, bad scalars). */
+int dsa_cache_append(const dsa_batch_t* batch, const uint16_t* k_new, const uint16_t* kv_new,
+                     uint8_t* k8_cache, float* k_scale, uint16_t* kv_cache, void* stream);
+
 /* Per-row top-k over scores[t, 0 .. v_t) ("MTP and sparse attention: NSA
  * and DSA", DSA bullet: each query keeps its 2048 highest-scoring tokens).
  *  scores  f32 [T, ld]; -0.0 ranks as +0.0; NaN ranks above +inf

@@ -20,7 +20,7 @@ DSA_STAGE_INDEX_SCORE, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_NUM_STAGES = 0, 
 PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 128, 128, 576, 512, 8192
 
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
-           "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
+           "dsa_cache_append", "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
 
 
 class DsaError(RuntimeError):
@@ -72,7 +72,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_step.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
                                       ctypes.POINTER(dsa_mla_inputs_t), i32,
                                       ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp, sz, vp, vp]
-        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step"):
+        L.dsa_cache_append.argtypes = [bp, vp, vp, vp, vp, vp, vp]
+        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
+                  "dsa_cache_append"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
         L.dsa_workspace_size.restype = sz
@@ -143,6 +145,11 @@ def dsa_index_score(batch: Batch, q8, q_scale, w, k8_cache, k_scale, scores, ld:
                     stream=None):
     _check(lib().dsa_index_score(batch.ref(), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8_cache),
                                  _ptr(k_scale), _ptr(scores), int(ld), _stream(stream)))
+
+
+def dsa_cache_append(batch: Batch, k_new, kv_new, k8_cache, k_scale, kv_cache, stream=None):
+    _check(lib().dsa_cache_append(batch.ref(), _ptr(k_new), _ptr(kv_new), _ptr(k8_cache),
+                                  _ptr(k_scale), _ptr(kv_cache), _stream(stream)))
 
 
 def dsa_topk(batch: Batch, scores, ld: int, k: int, idx, ws, ws_bytes: int, stream=None):

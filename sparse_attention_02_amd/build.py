@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip"]
 # per-file code-generation options: the indexer reads its MFMA results with
 # VALU right away, so they are kept in VGPRs instead of AGPRs
 FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

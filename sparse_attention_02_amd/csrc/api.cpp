@@ -159,6 +159,24 @@ int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_
   return e == hipSuccess ? DSA_OK : hip_fail(e, "index_score launch");
 }
 
+int dsa_cache_append(const dsa_batch_t* batch, const uint16_t* k_new, const uint16_t* kv_new,
+                     uint8_t* k8_cache, float* k_scale, uint16_t* kv_cache, void* stream) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (batch->num_tokens == 0 || batch->max_seqlen_k == 0) return DSA_OK;
+  if (!k_new || !kv_new || !k8_cache || !k_scale || !kv_cache)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  auto misaligned = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
+  if (misaligned(kv_new, 16) || misaligned(kv_cache, 16) || misaligned(k_new, 4) ||
+      misaligned(k8_cache, 2) || misaligned(k_scale, 4))
+    return fail(DSA_ERR_INVALID_ARG,
+                "kv_new / kv_cache need 16-byte, k_new / k_scale 4-byte, k8_cache 2-byte alignment");
+  hipError_t e = dsa::launch_cache_append(dsa::batch_args(*batch), k_new, kv_new, k8_cache, k_scale,
+                                          kv_cache, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "cache_append launch");
+}
+
 int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
              void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();

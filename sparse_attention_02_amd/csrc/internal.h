@@ -65,6 +65,9 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
 uint32_t* topk_hist1(const BatchArgs& b, void* ws);
 bool topk_supported(const BatchArgs& b, int k);
 
+hipError_t launch_cache_append(const BatchArgs& b, const uint16_t* k_new, const uint16_t* kv_new,
+                               uint8_t* k8, float* ks, uint16_t* kv, hipStream_t s);
+
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
                              const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,
                              int n_split, void* ws, hipStream_t s);

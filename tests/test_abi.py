@@ -86,6 +86,25 @@ def test_index_score_argument_checks(L):
         B.DSA_ERR_INVALID_ARG
 
 
+def test_cache_append_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    ok = (P, P, P, P, P)
+    for i in range(5):  # each tensor pointer NULL in turn
+        args = list(ok)
+        args[i] = None
+        assert L.dsa_cache_append(ctypes.byref(b), *args, None) == B.DSA_ERR_INVALID_ARG
+    # kv_new / kv_cache 16-byte, k_new / k_scale 4-byte, k8_cache 2-byte alignment
+    for i, off in ((1, 8), (4, 8), (0, 2), (3, 2), (2, 1)):
+        args = list(ok)
+        args[i] = P + off
+        assert L.dsa_cache_append(ctypes.byref(b), *args, None) == B.DSA_ERR_INVALID_ARG
+        assert "alignment" in _err(L)
+    empty = _batch(B_=0, T=0, max_q=0, max_seqlen_k=0, ptrs=False)
+    assert L.dsa_cache_append(ctypes.byref(empty), None, None, None, None, None, None) == B.DSA_OK
+    assert L.dsa_cache_append(None, *ok, None) == B.DSA_ERR_INVALID_ARG
+
+
 def test_sparse_mla_argument_checks(L):
     P = 0x1000
     b = _batch()

@@ -1,0 +1,173 @@
+"""Parity of the cache append (dsa_cache_append) with the oracle, through the
+C ABI.  Byte work: the FP8 codes, the fp32 scales (compared as bits) and the
+latent rows must equal the oracle's exactly, and every slot the step does not
+own must keep its previous contents."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_02_amd as dsa
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+P = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.lib()
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def _batch(n_q, L, rng, num_pages=None, bad_last_page=()):
+    """Requests of n_q new rows onto L cached tokens (rows included), with a
+    page table drawn from a shuffled pool; requests listed in bad_last_page
+    get an out-of-pool id for the page of their last row."""
+    n_q, L = np.asarray(n_q, np.int32), np.asarray(L, np.int32)
+    pages = [(int(l) + P - 1) // P for l in L]
+    total = sum(pages)
+    num_pages = num_pages or total + 3
+    pool = rng.permutation(num_pages)[:total].astype(np.int32)
+    maxp = max(max(pages), 1)
+    pt = np.full((len(L), maxp), -1, np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        pt[b, :n] = pool[off:off + n]
+        off += n
+        if b in bad_last_page and n:
+            pt[b, n - 1] = num_pages + 5
+    cu = np.concatenate([[0], np.cumsum(n_q)]).astype(np.int32)
+    return cu, L, pt, num_pages
+
+
+def _run(cu, L, pt, num_pages, k_new, kv_new, seed=0):
+    rng = np.random.default_rng(seed)
+    k8 = rng.integers(0, 256, (num_pages, P, 128)).astype(np.uint8)
+    ks = rng.normal(0, 1, (num_pages, P)).astype(np.float32)
+    kv = rng.integers(0, 1 << 16, (num_pages, P, 576)).astype(np.uint16)
+    meta = O.Meta(cu, L, pt)
+    ref = O.cache_append(meta, num_pages, k_new, kv_new, k8, ks, kv)
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    batch = dsa.Batch(dev(cu), dev(L), dev(pt), num_pages, int(max(np.diff(cu).max(), 1)),
+                      int(max(L.max(), 1)))
+    g_k8, g_ks, g_kv = dev(k8), dev(ks), dev(kv.view(np.int16))
+    dsa.dsa_cache_append(batch, dev(k_new.view(np.int16)), dev(kv_new.view(np.int16)), g_k8, g_ks,
+                         g_kv)
+    torch.cuda.synchronize()
+    got = (g_k8.cpu().numpy(), g_ks.cpu().numpy(), g_kv.cpu().numpy().view(np.uint16))
+    assert np.array_equal(got[0], ref[0]), np.argwhere(got[0] != ref[0])[:5]
+    assert np.array_equal(got[1].view(np.uint32), ref[1].view(np.uint32)), \
+        np.argwhere(got[1].view(np.uint32) != ref[1].view(np.uint32))[:5]
+    assert np.array_equal(got[2], ref[2])
+    return ref
+
+
+CASES = [
+    dict(n_q=[1], L=[1]),
+    dict(n_q=[2, 1, 3], L=[64, 65, 10]),
+    dict(n_q=[2, 2, 1, 5], L=[130, 5000, 0, 4100]),
+    dict(n_q=[1] * 9, L=[63, 64, 127, 128, 129, 700, 2048, 4097, 1]),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_cache_append_matches_oracle(ci):
+    case = CASES[ci]
+    rng = np.random.default_rng(100 + ci)
+    n_q = [n if l >= n else 0 for n, l in zip(case["n_q"], case["L"])]  # L = 0: padding request
+    cu, L, pt, num_pages = _batch(n_q, case["L"], rng)
+    T = int(cu[-1])
+    k_new = _bf16_bits(rng.normal(0, 1, (T, 128)) * rng.uniform(1e-3, 1e3, (T, 1)))
+    kv_new = rng.integers(0, 1 << 16, (T, 576)).astype(np.uint16)
+    _run(cu, L, pt, num_pages, k_new, kv_new, seed=ci)
+
+
+def test_cache_append_special_keys():
+    """Keys whose quotients hit every FP8 code and every midpoint between
+    neighbouring codes exactly (scale 1: each key holds 448), an all-zero
+    key, signed zeros, tiny and huge magnitudes."""
+    rng = np.random.default_rng(7)
+    vals = [O.e4m3_decode(c) for c in range(0x7F)]
+    mids = [(vals[c] + vals[c + 1]) / 2 for c in range(0x7E)]
+    grid = np.array(vals + mids + [-v for v in vals] + [-m for m in mids], np.float64)
+    rows = []
+    for i in range(0, len(grid), 127):
+        r = np.zeros(128)
+        r[:len(grid[i:i + 127])] = grid[i:i + 127]
+        r[127] = 448.0
+        rows.append(r)
+    k = _bf16_bits(np.array(rows))
+    exact = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(exact, np.array(rows))  # every value above is exact in bf16
+    extra = np.zeros((6, 128), np.float32)
+    extra[1, ::2] = -0.0
+    extra[2] = rng.normal(0, 1e-30, 128)
+    extra[3] = rng.normal(0, 1e30, 128)
+    extra[4] = rng.normal(0, 1, 128)
+    extra[4, 5] = 1e-20  # far below the key's smallest code
+    extra[5] = np.where(rng.random(128) < 0.5, 3.0, -3.0)
+    k = np.concatenate([k, _bf16_bits(extra)])
+    k[len(rows) + 1, ::2] = 0x8000  # -0.0 bit patterns
+    T = len(k)
+    cu, L, pt, num_pages = _batch([1] * T, [70 + 64 * i for i in range(T)], rng)
+    kv_new = rng.integers(0, 1 << 16, (T, 576)).astype(np.uint16)
+    _run(cu, L, pt, num_pages, k, kv_new)
+
+
+def test_cache_append_skips_invalid_pages_and_short_requests():
+    rng = np.random.default_rng(9)
+    # request 1's last page id lies outside the pool; request 2 is a padding
+    # request (no rows); request 3 caches fewer tokens than it has rows
+    n_q = [2, 3, 0, 3, 1]
+    L = [200, 90, 0, 2, 64]
+    cu, L, pt, num_pages = _batch(n_q, L, rng, bad_last_page=(1,))
+    T = int(cu[-1])
+    k_new = _bf16_bits(rng.normal(0, 1, (T, 128)))
+    kv_new = rng.integers(0, 1 << 16, (T, 576)).astype(np.uint16)
+    _run(cu, L, pt, num_pages, k_new, kv_new)
+
+
+def test_cache_append_decode_batch_at_full_size():
+    """The headline decode batch: 64 requests x 2 rows onto 131072 cached
+    tokens, the launch the bench times (the page pool holds only the pages
+    the new rows fall on, each request's own)."""
+    rng = np.random.default_rng(11)
+    B, n, Lc = 64, 2, 131072
+    maxp = Lc // P
+    num_pages = 2 * B + 7
+    pool = rng.permutation(num_pages).astype(np.int32)
+    pt = np.full((B, maxp), -1, np.int32)
+    pt[:, maxp - 1] = pool[:B]  # positions 131070 and 131071 share the last page
+    cu = np.arange(0, B * n + 1, n, dtype=np.int32)
+    L = np.full(B, Lc, np.int32)
+    T = B * n
+    k_new = _bf16_bits(rng.normal(0, 1, (T, 128)))
+    kv_new = _bf16_bits(rng.normal(0, 1 / 24, (T, 576)))
+    ref = _run(cu, L, pt, num_pages, k_new, kv_new)
+    # both rows of each request landed on its last page, slots 62 and 63
+    for b in range(0, B, 9):
+        pg = pt[b, maxp - 1]
+        assert np.array_equal(ref[2][pg, 62], kv_new[n * b]) and np.array_equal(ref[2][pg, 63],
+                                                                               kv_new[n * b + 1])
+
+
+def test_cache_append_rejects_misaligned_latent():
+    rng = np.random.default_rng(3)
+    cu, L, pt, num_pages = _batch([1], [5], rng)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    batch = dsa.Batch(dev(cu), dev(L), dev(pt), num_pages, 1, 5)
+    k = torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda")
+    kvn = torch.zeros(577, dtype=torch.bfloat16, device="cuda")[1:]  # 2-byte offset
+    k8 = torch.zeros((num_pages, P, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((num_pages, P), dtype=torch.float32, device="cuda")
+    kv = torch.zeros((num_pages, P, 576), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_cache_append(batch, k, kvn, k8, ks, kv)
