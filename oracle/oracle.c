@@ -437,3 +437,34 @@ void oracle_cache_append(const oracle_batch* bt, int32_t num_pages, int32_t D_id
     }
   }
 }
+
+/* ---- index transform -------------------------------------------------------
+ * "[SGLang] NSA": the top-k's positions are turned into the page-table
+ * indices the paged sparse kernel reads, or into offsets of a ragged KV
+ * buffer.  idx int32 [n_rows, k] holds logical positions (-1 padding) of the
+ * rows `rows`; out receives, per entry: the position itself (space 0), its
+ * slot page_table[b][s / page_size] * page_size + s % page_size, -1 for a
+ * page id outside [0, num_pages) (space 1), or kv_offsets[b] + s (space 2). */
+void oracle_transform_index(const oracle_batch* bt, int32_t num_pages, int32_t space,
+                            const int32_t* kv_offsets, const int32_t* idx, const int32_t* rows,
+                            int32_t n_rows, int32_t k, int32_t* out) {
+  for (int32_t i = 0; i < n_rows; ++i) {
+    const int32_t b = oracle_row_request(bt, rows[i]);
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t s = idx[(int64_t)i * k + j];
+      int32_t r = -1;
+      if (s >= 0 && b >= 0) {
+        if (space == 0) {
+          r = s;
+        } else if (space == 1) {
+          const int64_t page = bt->page_table[(int64_t)b * bt->max_pages + s / bt->page_size];
+          r = (page >= 0 && page < num_pages) ? (int32_t)(page * bt->page_size + s % bt->page_size)
+                                              : -1;
+        } else {
+          r = kv_offsets[b] + s;
+        }
+      }
+      out[(int64_t)i * k + j] = r;
+    }
+  }
+}

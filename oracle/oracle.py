@@ -64,6 +64,7 @@ def lib():
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_cache_append.argtypes = [bp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_transform_index.argtypes = [bp, i32, i32, vp, vp, vp, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -202,3 +203,15 @@ def selection_check(gpu_idx, sel, flags, K):
             if len(probs) > 8:
                 break
     return probs
+
+
+def transform_index(meta: Meta, num_pages: int, space: int, idx, rows, kv_offsets=None):
+    """Selections idx int32 [len(rows), k] (logical positions, -1 padding) in
+    index space 0 (logical), 1 (physical slot) or 2 (kv_offsets[b] + s)."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    rows = np.ascontiguousarray(rows, np.int32)
+    off = np.ascontiguousarray(kv_offsets if kv_offsets is not None else np.zeros(1), np.int32)
+    out = np.empty_like(idx)
+    lib().oracle_transform_index(meta.ref(), int(num_pages), int(space), _p(off), _p(idx),
+                                 _p(rows), len(rows), idx.shape[1], _p(out))
+    return out

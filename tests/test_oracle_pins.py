@@ -142,6 +142,57 @@ def test_cache_append_places_quantises_and_leaves_other_slots():
     assert np.all(kvo[~touched] == 0x1234)
 
 
+def test_transform_index_spaces():
+    rng = np.random.default_rng(21)
+    L = np.array([300, 130, 0, 64], np.int32)
+    n = np.array([2, 1, 0, 1])
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    pages = (L + 63) // 64
+    num_pages = int(pages.sum()) + 2
+    perm = rng.permutation(num_pages).astype(np.int32)
+    pt = np.full((4, int(pages.max())), -1, np.int32)
+    off = 0
+    for b, p_ in enumerate(pages):
+        pt[b, :p_] = perm[off:off + p_]
+        off += p_
+    pt[1, 1] = num_pages + 3  # positions 64..127 of request 1 lie on a page outside the pool
+    meta = O.Meta(cu, L, pt)
+    rows = np.arange(int(cu[-1]), dtype=np.int32)
+    k = 8
+    idx = np.full((len(rows), k), -1, np.int32)
+    req = np.searchsorted(cu, rows, side="right") - 1
+    for i, t in enumerate(rows):
+        v = meta.visible(int(t))
+        sel = np.sort(rng.choice(v, size=min(k - 1, v), replace=False))
+        idx[i, :len(sel)] = sel
+    logical = O.transform_index(meta, num_pages, 0, idx, rows)
+    assert np.array_equal(logical, idx)
+    paged = O.transform_index(meta, num_pages, 1, idx, rows)
+    inv = np.argsort(perm)  # pool page -> its place in the pool permutation
+    for i, t in enumerate(rows):
+        b = req[i]
+        for j in range(k):
+            s_ = idx[i, j]
+            if s_ < 0:
+                assert paged[i, j] == -1
+            elif b == 1 and s_ // 64 == 1:
+                assert paged[i, j] == -1  # page outside the pool
+            else:
+                # the slot's page is the request's page holding the position
+                # (recovered through the pool permutation), same offset in it
+                pg, o = divmod(int(paged[i, j]), 64)
+                place = inv[pg] - int(pages[:b].sum())
+                assert place == s_ // 64 and o == s_ % 64
+    ident = O.Meta(cu, L, np.arange(pt.size, dtype=np.int32).reshape(pt.shape) * 0
+                   + np.arange(pt.shape[1], dtype=np.int32)[None, :])
+    assert np.array_equal(O.transform_index(ident, pt.shape[1], 1, idx, rows), idx)
+    starts = np.concatenate([[0], np.cumsum(L)[:-1]]).astype(np.int32)
+    rag = O.transform_index(meta, num_pages, 2, idx, rows, starts)
+    live = idx >= 0
+    assert np.array_equal(rag[live] - starts[req][:, None].repeat(k, 1)[live], idx[live])
+    assert np.all(rag[~live] == -1) and np.all(rag[live] < int(L.sum()))
+
+
 # ------------------------------------------------------------- visibility
 
 def test_visibility_worked_example():
