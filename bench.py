@@ -310,6 +310,46 @@ def append_measure(iters=200):
     return res
 
 
+def index_space_measure(b, d, iters=20):
+    """Top-k + attention with logical positions against the fused transform
+    to physical slots + attention over slots (no page-table lookups in the
+    attention), on the bench workload's scores."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    import synth
+    T, k = b.T, synth.TOPK
+    ld = (int(b.max_seqlen_k) + 63) // 64 * 64
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_score(d.meta, d.q8, d.q_scale, d.w, d.k8[0], d.k_scale[0], scores, ld)
+    tk = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, d.meta, k)
+    mk = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, d.meta, k)
+    ws_t = torch.empty(tk, dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(max(mk, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+
+    def logical():
+        dsa.dsa_topk(d.meta, scores, ld, k, idx, ws_t, tk)
+        dsa.dsa_sparse_mla_decode(d.meta, d.q[0], d.kv[0], idx, k, synth.SM_SCALE, out, lse, 0,
+                                  ws_m, mk)
+
+    def paged():
+        dsa.dsa_topk_transform(d.meta, scores, ld, k, dsa.DSA_IDX_PAGED, None, idx, ws_t, tk)
+        dsa.dsa_sparse_mla_decode_paged(d.meta, d.q[0], d.kv[0], idx, k, synth.SM_SCALE, out, lse,
+                                        0, ws_m, mk)
+
+    res = {"logical_ms": [], "paged_ms": []}
+    for _ in range(3):  # interleaved rounds
+        res["logical_ms"].append(wall_ms(logical, iters))
+        res["paged_ms"].append(wall_ms(paged, iters))
+    res = {key: min(v) for key, v in res.items()}
+    del scores, ws_t, ws_m, idx, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def mli_measure(steps):
     """Two-stream MLI step vs the same kernels back to back on one stream."""
     import numpy as np
@@ -386,6 +426,7 @@ def main():
     log(f"step {ms_step:.3f} ms | indexer {ms_idx:.3f} ms {idx_gbs:.0f} GB/s | top-k "
         f"{ms_topk:.3f} ms | attention {ms_attn:.3f} ms {attn_gbs:.0f} GB/s | step "
         f"{step_gbs:.0f} GB/s")
+    space = index_space_measure(b, d) if args.extras else None
     del step, d
     torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth()
@@ -424,6 +465,8 @@ def main():
         log(f"mli {result['mli']}")
         result["cache_append"] = append_measure()
         log(f"cache append {result['cache_append']}")
+        result["index_space"] = space
+        log(f"top-k + attention, logical vs physical-slot indices {result['index_space']}")
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         rows = list(range(min(args.cpu_rows, T)))

@@ -143,6 +143,28 @@ int dsa_cache_append(const dsa_batch_t* batch, const uint16_t* k_new, const uint
 int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
              void* ws, size_t ws_bytes, void* stream);
 
+/* Index spaces for a selection ("[SGLang] NSA": the top-k's positions are
+ * turned into page-table indices for the paged sparse kernel, or into
+ * offsets of a ragged KV buffer, by a transform fused with the top-k). */
+enum {
+  DSA_IDX_LOGICAL = 0, /* positions within the request (0 .. v_t-1) */
+  DSA_IDX_PAGED = 1,   /* physical slots: page_table[b][p / 64] * 64 + p % 64
+                          (-1 where the page id is outside [0, num_pages)) */
+  DSA_IDX_RAGGED = 2   /* kv_offsets[b] + p: a buffer holding each request's
+                          tokens contiguously from kv_offsets[b] on */
+};
+
+/* Top-k fused with the transform of its output into an index space: the
+ * selection of dsa_topk (same set, same ascending order of the positions
+ * behind the entries), each entry reported in `space`; -1 padding as
+ * dsa_topk.  kv_offsets: int32 [B], read for DSA_IDX_RAGGED only (the
+ * caller keeps kv_offsets[b] + v_t within int32).
+ * Errors: as dsa_topk, and INVALID_ARG for an unknown space or a NULL
+ * kv_offsets with DSA_IDX_RAGGED. */
+int dsa_topk_transform(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k,
+                       int32_t space, const int32_t* kv_offsets, int32_t* idx, void* ws,
+                       size_t ws_bytes, void* stream);
+
 /* Sparse absorbed-MLA decode over selected tokens ("MTP and sparse
  * attention: NSA and DSA", DSA bullet and per-pair cost; split-KV online
  * softmax + LSE merge per "Deepseek Details", DSA, stages 2-3).
@@ -162,6 +184,18 @@ int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t 
 int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
                           const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
                           float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream);
+
+/* dsa_sparse_mla_decode over physical slots (DSA_IDX_PAGED, as
+ * dsa_topk_transform writes them): slots int32 [T, k]; entries < 0 or
+ * >= num_pages * 64 are skipped and the rest must be distinct within a row;
+ * no page-table lookup is made (the batch's page table may be NULL when
+ * max_seqlen_k is 0), and the caller vouches that the slots are the row's
+ * selection.  Output and errors as dsa_sparse_mla_decode, whose workspace
+ * size it shares. */
+int dsa_sparse_mla_decode_paged(const dsa_batch_t* batch, const uint16_t* q,
+                                const uint16_t* kv_cache, const int32_t* slots, int32_t k,
+                                float sm_scale, uint16_t* out, float* lse, int32_t n_split,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Indexer inputs of one layer (device pointers, layouts as dsa_index_score). */
 typedef struct {

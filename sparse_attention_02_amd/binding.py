@@ -17,10 +17,12 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP = 1, 2, 3
 DSA_MODE_FUSED, DSA_MODE_MLI = 0, 1
 DSA_STAGE_INDEX_SCORE, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_NUM_STAGES = 0, 1, 2, 3
+DSA_IDX_LOGICAL, DSA_IDX_PAGED, DSA_IDX_RAGGED = 0, 1, 2
 PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 128, 128, 576, 512, 8192
 
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
-           "dsa_cache_append", "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
+           "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
+           "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
 
 
 class DsaError(RuntimeError):
@@ -73,8 +75,10 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(dsa_mla_inputs_t), i32,
                                       ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp, sz, vp, vp]
         L.dsa_cache_append.argtypes = [bp, vp, vp, vp, vp, vp, vp]
+        L.dsa_topk_transform.argtypes = [bp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
+        L.dsa_sparse_mla_decode_paged.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
         for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
-                  "dsa_cache_append"):
+                  "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
         L.dsa_workspace_size.restype = sz
@@ -155,6 +159,21 @@ def dsa_cache_append(batch: Batch, k_new, kv_new, k8_cache, k_scale, kv_cache, s
 def dsa_topk(batch: Batch, scores, ld: int, k: int, idx, ws, ws_bytes: int, stream=None):
     _check(lib().dsa_topk(batch.ref(), _ptr(scores), int(ld), int(k), _ptr(idx), _ptr(ws),
                           int(ws_bytes), _stream(stream)))
+
+
+def dsa_topk_transform(batch: Batch, scores, ld: int, k: int, space: int, kv_offsets, idx, ws,
+                       ws_bytes: int, stream=None):
+    _check(lib().dsa_topk_transform(batch.ref(), _ptr(scores), int(ld), int(k), int(space),
+                                    _ptr(kv_offsets), _ptr(idx), _ptr(ws), int(ws_bytes),
+                                    _stream(stream)))
+
+
+def dsa_sparse_mla_decode_paged(batch: Batch, q, kv_cache, slots, k: int, sm_scale: float, out,
+                                lse, n_split: int, ws, ws_bytes: int, stream=None):
+    _check(lib().dsa_sparse_mla_decode_paged(batch.ref(), _ptr(q), _ptr(kv_cache), _ptr(slots),
+                                             int(k), float(sm_scale), _ptr(out), _ptr(lse),
+                                             int(n_split), _ptr(ws), int(ws_bytes),
+                                             _stream(stream)))
 
 
 def dsa_sparse_mla_decode(batch: Batch, q, kv_cache, idx, k: int, sm_scale: float, out, lse,

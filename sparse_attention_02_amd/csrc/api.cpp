@@ -177,28 +177,34 @@ int dsa_cache_append(const dsa_batch_t* batch, const uint16_t* k_new, const uint
   return e == hipSuccess ? DSA_OK : hip_fail(e, "cache_append launch");
 }
 
-int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
-             void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+int topk_common(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t space,
+                const int32_t* kv_offsets, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   int rc = check_batch(batch);
   if (rc) return rc;
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
   if (ld < batch->max_seqlen_k) return fail(DSA_ERR_INVALID_ARG, "ld < max_seqlen_k");
+  if (space != DSA_IDX_LOGICAL && space != DSA_IDX_PAGED && space != DSA_IDX_RAGGED)
+    return fail(DSA_ERR_INVALID_ARG, "unknown index space");
   if (batch->num_tokens == 0) return DSA_OK;
   if (!idx || (!scores && batch->max_seqlen_k > 0))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (space == DSA_IDX_RAGGED && !kv_offsets)
+    return fail(DSA_ERR_INVALID_ARG, "ragged indices need kv_offsets");
   if (!dsa::topk_supported(dsa::batch_args(*batch), k))
     return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
   const size_t need = dsa::topk_ws_layout(dsa::batch_args(*batch)).total;
   if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "top-k workspace too small");
   hipError_t e = dsa::launch_topk(dsa::batch_args(*batch), scores, ld, k, idx, ws,
-                                  (hipStream_t)stream);
+                                  (hipStream_t)stream, space, kv_offsets);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");
 }
 
-int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
-                          const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
-                          float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream) {
+int mla_common(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
+               const int32_t* idx, int32_t k, float sm_scale, uint16_t* out, float* lse,
+               int32_t n_split, void* ws, size_t ws_bytes, void* stream, bool paged) {
   g_err.clear();
   int rc = check_batch(batch);
   if (rc) return rc;
@@ -207,15 +213,43 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uin
   rc = resolve_splits(batch, k, n_split, &used);
   if (rc) return rc;
   if (batch->num_tokens == 0) return DSA_OK;
-  if (!q || !idx || !out || (!kv_cache && batch->max_seqlen_k > 0))
+  if (!q || !idx || !out || (!kv_cache && (batch->max_seqlen_k > 0 || paged)))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   const dsa::BatchArgs a = dsa::batch_args(*batch);
   const size_t need = dsa::mla_ws_layout(a, used).total;
   if (need > 0 && (ws_bytes < need || !ws))
     return fail(DSA_ERR_WORKSPACE, "attention workspace too small");
   hipError_t e = dsa::launch_sparse_mla(a, q, kv_cache, idx, k, sm_scale, out, lse, used, ws,
-                                        (hipStream_t)stream);
+                                        (hipStream_t)stream, paged);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA launch");
+}
+
+}  // namespace
+
+int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
+             void* ws, size_t ws_bytes, void* stream) {
+  return topk_common(batch, scores, ld, k, DSA_IDX_LOGICAL, nullptr, idx, ws, ws_bytes, stream);
+}
+
+int dsa_topk_transform(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k,
+                       int32_t space, const int32_t* kv_offsets, int32_t* idx, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return topk_common(batch, scores, ld, k, space, kv_offsets, idx, ws, ws_bytes, stream);
+}
+
+int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
+                          const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
+                          float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream) {
+  return mla_common(batch, q, kv_cache, idx, k, sm_scale, out, lse, n_split, ws, ws_bytes, stream,
+                    false);
+}
+
+int dsa_sparse_mla_decode_paged(const dsa_batch_t* batch, const uint16_t* q,
+                                const uint16_t* kv_cache, const int32_t* slots, int32_t k,
+                                float sm_scale, uint16_t* out, float* lse, int32_t n_split,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return mla_common(batch, q, kv_cache, slots, k, sm_scale, out, lse, n_split, ws, ws_bytes, stream,
+                    true);
 }
 
 int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,

@@ -56,20 +56,24 @@ hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float
                               float* scores, int64_t ld, uint32_t* hist, hipStream_t s);
 
 // Whole top-k: zero, histogram, threshold, collect, final.
+// space: DSA_IDX_LOGICAL / PAGED / RAGGED (kv_off [B] for RAGGED, else unused)
 hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, hipStream_t s);
+                       void* ws, hipStream_t s, int space = DSA_IDX_LOGICAL,
+                       const int32_t* kv_off = nullptr);
 // Pieces used by the fused step, whose indexer builds the histogram.
 hipError_t launch_topk_zero(const BatchArgs& b, void* ws, hipStream_t s);
 hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t ld, int k,
-                              int32_t* idx, void* ws, hipStream_t s);
+                              int32_t* idx, void* ws, hipStream_t s, int space = DSA_IDX_LOGICAL,
+                              const int32_t* kv_off = nullptr);
 uint32_t* topk_hist1(const BatchArgs& b, void* ws);
 bool topk_supported(const BatchArgs& b, int k);
 
 hipError_t launch_cache_append(const BatchArgs& b, const uint16_t* k_new, const uint16_t* kv_new,
                                uint8_t* k8, float* ks, uint16_t* kv, hipStream_t s);
 
+// paged: idx holds physical slots (DSA_IDX_PAGED) instead of logical positions
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
                              const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,
-                             int n_split, void* ws, hipStream_t s);
+                             int n_split, void* ws, hipStream_t s, bool paged = false);
 
 }  // namespace dsa

@@ -280,9 +280,21 @@ __device__ uint32_t radix_select(int n, uint32_t need, Get get, uint32_t* h, uin
   return prefix;
 }
 
+// The index a selected position is reported as: itself (DSA_IDX_LOGICAL),
+// its physical slot through the page table (DSA_IDX_PAGED; -1 for a page id
+// outside the pool), or its offset in a ragged buffer that holds request b's
+// tokens from kv_off[b] on (DSA_IDX_RAGGED).
+__device__ __forceinline__ int32_t index_in_space(const BatchArgs& b, int bi, int space,
+                                                  const int32_t* kv_off, int pos) {
+  if (space == DSA_IDX_PAGED) return (int32_t)slot_of(b, bi, pos);
+  if (space == DSA_IDX_RAGGED) return kv_off[bi] + pos;
+  return pos;
+}
+
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     BatchArgs b, int k, const int32_t* __restrict__ ctrl, const uint32_t* __restrict__ hist2,
-    int32_t* __restrict__ idx, const uint2* __restrict__ cand, int64_t cand_stride) {
+    int32_t* __restrict__ idx, const uint2* __restrict__ cand, int64_t cand_stride, int space,
+    const int32_t* __restrict__ kv_off) {
   __shared__ uint32_t bitmap[kBitmapWords];
   __shared__ int32_t sel[kSortCap];
   __shared__ uint32_t h[kTopkBins];
@@ -292,7 +304,8 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   __shared__ uint32_t s_above;
   __shared__ int32_t s_count;
   const int t = blockIdx.x;
-  const int v = row_len(b, t);
+  const int bi = row_request(b.cu, b.B, t);
+  const int v = row_visible(b, bi, t);
   const int K = min(k, v);
   const int n_above = min(ctrl[t * kCtrlWords + kCtrlAbove], K);
   const int nc = ctrl[t * kCtrlWords + kCtrlCand];
@@ -368,7 +381,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
       while (m) {
         const int bit = __ffs(m) - 1;
         m &= m - 1;
-        if (at < (uint32_t)K) out[at] = (w << 5) + bit;
+        if (at < (uint32_t)K) out[at] = index_in_space(b, bi, space, kv_off, (w << 5) + bit);
         ++at;
       }
     }
@@ -409,7 +422,8 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < k; i += kFinalThreads) out[i] = i < K ? sel[i] : -1;
+  for (int i = threadIdx.x; i < k; i += kFinalThreads)
+    out[i] = i < K ? index_in_space(b, bi, space, kv_off, sel[i]) : -1;
 }
 
 }  // namespace
@@ -448,7 +462,8 @@ hipError_t launch_topk_zero(const BatchArgs& b, void* ws, hipStream_t s) {
 }
 
 hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t ld, int k,
-                              int32_t* idx, void* ws, hipStream_t s) {
+                              int32_t* idx, void* ws, hipStream_t s, int space,
+                              const int32_t* kv_off) {
   if (b.T == 0) return hipSuccess;
   const TopkWs L = topk_ws_layout(b);
   char* base = static_cast<char*>(ws);
@@ -461,12 +476,12 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
   hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k, hist1,
                      ctrl, idx, cand, (int64_t)b.max_seqlen_k, hist2);
   hipLaunchKernelGGL(topk_final_kernel, dim3(b.T), dim3(kFinalThreads), 0, s, b, k, ctrl, hist2,
-                     idx, cand, (int64_t)b.max_seqlen_k);
+                     idx, cand, (int64_t)b.max_seqlen_k, space, kv_off);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, hipStream_t s) {
+                       void* ws, hipStream_t s, int space, const int32_t* kv_off) {
   if (b.T == 0) return hipSuccess;
   hipError_t e = launch_topk_zero(b, ws, s);
   if (e != hipSuccess) return e;
@@ -475,7 +490,7 @@ hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int 
                      topk_hist1(b, ws));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_select(b, scores, ld, k, idx, ws, s);
+  return launch_topk_select(b, scores, ld, k, idx, ws, s, space, kv_off);
 }
 
 }  // namespace dsa

@@ -105,6 +105,33 @@ def test_cache_append_argument_checks(L):
     assert L.dsa_cache_append(None, *ok, None) == B.DSA_ERR_INVALID_ARG
 
 
+def test_topk_transform_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    need = L.dsa_workspace_size(B.DSA_OP_TOPK, ctypes.byref(b), 16, 0)
+    for space in (-1, 3):
+        assert L.dsa_topk_transform(ctypes.byref(b), P, 300, 16, space, P, P, P, need, None) == \
+            B.DSA_ERR_INVALID_ARG
+        assert "space" in _err(L)
+    assert L.dsa_topk_transform(ctypes.byref(b), P, 300, 16, B.DSA_IDX_RAGGED, None, P, P, need,
+                                None) == B.DSA_ERR_INVALID_ARG
+    assert "kv_offsets" in _err(L)
+    assert L.dsa_topk_transform(ctypes.byref(b), P, 300, 16, B.DSA_IDX_PAGED, None, P, P,
+                                need - 1, None) == B.DSA_ERR_WORKSPACE
+
+
+def test_sparse_mla_paged_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    assert L.dsa_sparse_mla_decode_paged(ctypes.byref(b), P, P, P, 0, 0.1, P, None, 0, P, 1 << 30,
+                                         None) == B.DSA_ERR_INVALID_ARG
+    assert L.dsa_sparse_mla_decode_paged(ctypes.byref(b), P, None, P, 16, 0.1, P, None, 1, P,
+                                         1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    need = L.dsa_workspace_size(B.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 4)
+    assert L.dsa_sparse_mla_decode_paged(ctypes.byref(b), P, P, P, 2048, 0.1, P, None, 4, P,
+                                         need - 1, None) == B.DSA_ERR_WORKSPACE
+
+
 def test_sparse_mla_argument_checks(L):
     P = 0x1000
     b = _batch()
@@ -165,7 +192,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("DSA_MODE_FUSED", "DSA_MODE_MLI", "DSA_STAGE_INDEX_SCORE", "DSA_STAGE_TOPK",
                  "DSA_STAGE_ATTENTION", "DSA_NUM_STAGES", "DSA_OP_TOPK", "DSA_OP_SPARSE_MLA",
-                 "DSA_OP_DECODE_STEP"):
+                 "DSA_OP_DECODE_STEP", "DSA_IDX_LOGICAL", "DSA_IDX_PAGED", "DSA_IDX_RAGGED"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(B, name), name
 
