@@ -468,3 +468,31 @@ void oracle_transform_index(const oracle_batch* bt, int32_t num_pages, int32_t s
     }
   }
 }
+
+/* ---- multi-layer schedule -------------------------------------------------
+ * "Multi-layer Indexer: Overlapping Selection and Attention in DeepSeek
+ * Sparse Attention", abstract: IndexCache keeps an indexer on a fraction 1/r
+ * of the layers (here layers l with l % r == 0) and the other layers reuse
+ * the latest selection; MLI lets each layer attend the previous indexer
+ * layer's selection so that its own indexer runs concurrently with its
+ * attention.  For each layer: produces[l] = the number of the selection it
+ * makes (its rank among the indexer layers) or -1, and attends[l] = the
+ * number of the selection its attention reads.  Walks the layers in order,
+ * keeping the latest selection made and the one before it. */
+void oracle_layer_schedule(int32_t n_layers, int32_t r, int32_t mli, int32_t* produces,
+                           int32_t* attends) {
+  int32_t made = 0;       /* selections made so far */
+  int32_t latest = -1;    /* the newest selection, before this layer's own */
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const int keeps = (l % r) == 0;
+    produces[l] = keeps ? made : -1;
+    if (keeps) {
+      /* MLI: attend the selection before this layer's own, when there is one */
+      attends[l] = (mli && latest >= 0) ? latest : made;
+      latest = made;
+      ++made;
+    } else {
+      attends[l] = latest;
+    }
+  }
+}

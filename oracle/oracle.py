@@ -65,6 +65,7 @@ def lib():
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_cache_append.argtypes = [bp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_transform_index.argtypes = [bp, i32, i32, vp, vp, vp, i32, i32, vp]
+        L.oracle_layer_schedule.argtypes = [i32, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -215,3 +216,13 @@ def transform_index(meta: Meta, num_pages: int, space: int, idx, rows, kv_offset
     lib().oracle_transform_index(meta.ref(), int(num_pages), int(space), _p(off), _p(idx),
                                  _p(rows), len(rows), idx.shape[1], _p(out))
     return out
+
+
+def layer_schedule(n_layers: int, retention: int, mli: bool):
+    """(produces, attends) per layer: the selection a layer makes (-1: none)
+    and the selection its attention reads, numbered in the order made."""
+    produces = np.empty(n_layers, np.int32)
+    attends = np.empty(n_layers, np.int32)
+    lib().oracle_layer_schedule(int(n_layers), int(retention), int(bool(mli)), _p(produces),
+                                _p(attends))
+    return produces, attends

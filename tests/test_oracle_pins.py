@@ -193,6 +193,33 @@ def test_transform_index_spaces():
     assert np.all(rag[~live] == -1) and np.all(rag[live] < int(L.sum()))
 
 
+def test_layer_schedule_indexcache_and_mli():
+    # every layer keeps an indexer, no MLI: each layer attends its own selection
+    pr, at = O.layer_schedule(5, 1, False)
+    assert pr.tolist() == [0, 1, 2, 3, 4] and at.tolist() == [0, 1, 2, 3, 4]
+    # MLI alone (the two-stream step): layer l attends layer l-1's selection
+    pr, at = O.layer_schedule(5, 1, True)
+    assert pr.tolist() == [0, 1, 2, 3, 4] and at.tolist() == [0, 0, 1, 2, 3]
+    # IndexCache at 1/4: layers 0 and 4 keep an indexer, the rest reuse
+    pr, at = O.layer_schedule(8, 4, False)
+    assert pr.tolist() == [0, -1, -1, -1, 1, -1, -1, -1]
+    assert at.tolist() == [0, 0, 0, 0, 1, 1, 1, 1]
+    # composed: layer 4 attends selection 0 while making selection 1
+    pr, at = O.layer_schedule(9, 4, True)
+    assert at.tolist() == [0, 0, 0, 0, 0, 1, 1, 1, 1]
+    for n, r in ((12, 1), (12, 2), (12, 4), (13, 8), (3, 32)):
+        for mli in (False, True):
+            pr, at = O.layer_schedule(n, r, mli)
+            # a fraction 1/r of the layers keeps an indexer
+            assert (pr >= 0).sum() == -(-n // r)
+            # no layer reads a selection made after it; every one is made
+            made_at = {int(j): l for l, j in enumerate(pr) if j >= 0}
+            assert all(made_at[int(j)] <= l for l, j in enumerate(at))
+            # with MLI no indexer layer but the first waits for its own scan
+            if mli:
+                assert all(at[l] != pr[l] for l in range(1, n) if pr[l] >= 0)
+
+
 # ------------------------------------------------------------- visibility
 
 def test_visibility_worked_example():
