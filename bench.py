@@ -376,8 +376,46 @@ def mli_measure(steps):
     res = {"workload": b.name, "query_rows": b.T, "ms_one_stream": ms_seq,
            "ms_two_streams": ms_mli, "speedup": ms_seq / ms_mli,
            "overlap_mean": float(np.mean(ov)), "overlap_min": float(np.min(ov))}
+    res["layers"] = layers_measure(b, d, steps)
     del first, seq, mli, d
     torch.cuda.empty_cache()
+    return res
+
+
+def layers_measure(b, d, steps, n_layers=8):
+    """An n_layers stack (alternating the workload's two layers) under the
+    multi-layer indexer schedule: every layer indexed one stream at a time
+    (retention 1, no MLI: the unmodified model), and IndexCache retention
+    1/r with and without MLI."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    import synth
+    T, k = b.T, synth.TOPK
+    outs = [torch.empty((T, 128, 512), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    lses = [torch.empty((T, 128), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_DECODE_STEP, d.meta, k, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sel = torch.empty((n_layers, T, k), dtype=torch.int32, device="cuda")
+    aux = torch.cuda.Stream()
+    layers = []
+    for i in range(n_layers):
+        li = i % len(d.k8)
+        layers.append(dict(ix=dict(q8=d.q8, q_scale=d.q_scale, w=d.w, k8_cache=d.k8[li],
+                                   k_scale=d.k_scale[li]),
+                           mla=dict(q=d.q[li], kv_cache=d.kv[li], sm_scale=synth.SM_SCALE),
+                           out=outs[i], lse=lses[i]))
+    res = {"layers": n_layers}
+    for r in (1, 2, 4):
+        for mli in (0, 1):
+            def run(r=r, mli=mli):
+                dsa.dsa_decode_layers(d.meta, layers, k, r, mli, 0, sel, ws, ws_bytes,
+                                      stream_aux=aux if mli else None)
+            res[f"r{r}_mli{mli}_ms"] = wall_ms(run, max(3, steps // 4))
+    base = res["r1_mli0_ms"]
+    res["speedup_vs_every_layer"] = {key[:-3]: base / v for key, v in res.items()
+                                     if key.endswith("_ms")}
+    del outs, lses, ws, sel
     return res
 
 

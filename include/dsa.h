@@ -259,6 +259,38 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
                     int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                     void* stream_main, void* stream_aux);
 
+/* One layer of a multi-layer decode (device pointers, layouts as above). */
+typedef struct {
+  dsa_indexer_inputs_t ix; /* read on the layers that keep an indexer only */
+  dsa_mla_inputs_t mla;
+  uint16_t* out;           /* bf16 [T, 128, 512] out */
+  float* lse;              /* f32 [T, 128] out, or NULL */
+} dsa_layer_t;
+
+/* A stack of n_layers layers under a multi-layer indexer schedule ("Multi-
+ * layer Indexer: Overlapping Selection and Attention in DeepSeek Sparse
+ * Attention", abstract: IndexCache keeps the indexer on a fraction 1/r of
+ * the layers and the others reuse the latest selection; MLI lets a layer
+ * attend the previous indexer layer's selection so that its own indexer runs
+ * concurrently with its attention; the two compose).
+ * Layer l keeps an indexer iff l % retention == 0; its selection (as
+ * dsa_topk) is written to sel[l / retention].  Layer l attends
+ *   - with mli = 0: sel[l / retention] (on an indexer layer, its own, made
+ *     first);
+ *   - with mli = 1: sel[l / retention - 1] on an indexer layer l > 0 (its own
+ *     indexer + top-k run meanwhile on stream_aux, as DSA_MODE_MLI), else
+ *     sel[l / retention] (layer 0 selects first, then attends its own).
+ * retention = 1 with mli = 0 is n_layers fused decode steps.
+ *  layers   n_layers entries
+ *  sel      int32 [ceil(n_layers / retention), T, k] out
+ *  ws       >= dsa_workspace_size(DSA_OP_DECODE_STEP, batch, k, n_split)
+ *  stream_aux  used when mli = 1 (non-NULL, different from stream_main)
+ * Every pointer of every layer is checked before anything is enqueued.
+ * Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED, HIP. */
+int dsa_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_layer_t* layers,
+                      int32_t k, int32_t retention, int32_t mli, int32_t n_split, int32_t* sel,
+                      void* ws, size_t ws_bytes, void* stream_main, void* stream_aux);
+
 typedef enum {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA = 2,

@@ -22,6 +22,7 @@ PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 12
 
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
            "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
+           "dsa_decode_layers",
            "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
 
 
@@ -47,6 +48,11 @@ class dsa_indexer_inputs_t(ctypes.Structure):
 class dsa_mla_inputs_t(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("kv_cache", ctypes.c_void_p),
                 ("sm_scale", ctypes.c_float)]
+
+
+class dsa_layer_t(ctypes.Structure):
+    _fields_ = [("ix", dsa_indexer_inputs_t), ("mla", dsa_mla_inputs_t),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 class dsa_step_opts_t(ctypes.Structure):
@@ -77,8 +83,11 @@ def lib() -> ctypes.CDLL:
         L.dsa_cache_append.argtypes = [bp, vp, vp, vp, vp, vp, vp]
         L.dsa_topk_transform.argtypes = [bp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_sparse_mla_decode_paged.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
+        L.dsa_decode_layers.argtypes = [bp, i32, ctypes.POINTER(dsa_layer_t), i32, i32, i32, i32,
+                                        vp, vp, sz, vp, vp]
         for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
-                  "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged"):
+                  "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
+                  "dsa_decode_layers"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
         L.dsa_workspace_size.restype = sz
@@ -202,3 +211,23 @@ def dsa_decode_step(batch: Batch, ix: dict, mla: dict, k: int, mode: int, n_spli
     _check(lib().dsa_decode_step(batch.ref(), ctypes.byref(ixs), ctypes.byref(ms), int(k),
                                  ctypes.byref(opts), _ptr(idx_out), _ptr(out), _ptr(lse),
                                  _ptr(ws), int(ws_bytes), _stream(stream_main), aux))
+
+
+def dsa_decode_layers(batch: Batch, layers: list, k: int, retention: int, mli: int, n_split: int,
+                      sel, ws, ws_bytes: int, stream_main=None, stream_aux=None):
+    """layers: dicts with ix (q8, q_scale, w, k8_cache, k_scale; may be None on
+    layers without an indexer), mla (q, kv_cache, sm_scale), out and lse."""
+    arr = (dsa_layer_t * len(layers))()
+    for i, ly in enumerate(layers):
+        ix = ly.get("ix") or {}
+        arr[i].ix = dsa_indexer_inputs_t(_ptr(ix.get("q8")), _ptr(ix.get("q_scale")),
+                                         _ptr(ix.get("w")), _ptr(ix.get("k8_cache")),
+                                         _ptr(ix.get("k_scale")))
+        mla = ly["mla"]
+        arr[i].mla = dsa_mla_inputs_t(_ptr(mla["q"]), _ptr(mla["kv_cache"]), float(mla["sm_scale"]))
+        arr[i].out = _ptr(ly["out"])
+        arr[i].lse = _ptr(ly.get("lse"))
+    aux = None if stream_aux is None else _stream(stream_aux)
+    _check(lib().dsa_decode_layers(batch.ref(), len(layers), arr, int(k), int(retention), int(mli),
+                                   int(n_split), _ptr(sel), _ptr(ws), int(ws_bytes),
+                                   _stream(stream_main), aux))

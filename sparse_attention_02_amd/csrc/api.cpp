@@ -126,6 +126,67 @@ int32_t dsa_default_splits(const dsa_batch_t* batch, int32_t k) {
   return dsa::default_splits(dsa::batch_args(*batch), k);
 }
 
+int dsa_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_layer_t* layers,
+                      int32_t k, int32_t retention, int32_t mli, int32_t n_split, int32_t* sel,
+                      void* ws, size_t ws_bytes, void* stream_main, void* stream_aux) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (n_layers < 1 || !layers) return fail(DSA_ERR_INVALID_ARG, "need at least one layer");
+  if (retention < 1) return fail(DSA_ERR_INVALID_ARG, "retention must be >= 1");
+  if (mli != 0 && mli != 1) return fail(DSA_ERR_INVALID_ARG, "mli must be 0 or 1");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  if (mli && (!stream_aux || stream_aux == stream_main))
+    return fail(DSA_ERR_INVALID_ARG, "MLI needs a second stream");
+  int used = 1;
+  rc = resolve_splits(batch, k, n_split, &used);
+  if (rc) return rc;
+  if (batch->num_tokens == 0) return DSA_OK;
+  if (!sel) return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const bool keys = batch->max_seqlen_k > 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    if (!L.out || !L.mla.q || (keys && !L.mla.kv_cache))
+      return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer in a layer");
+    if (l % retention == 0 &&
+        (!L.ix.q8 || !L.ix.q_scale || !L.ix.w || (keys && (!L.ix.k8_cache || !L.ix.k_scale))))
+      return fail(DSA_ERR_INVALID_ARG, "NULL indexer pointer in an indexer layer");
+  }
+  if (!dsa::topk_supported(dsa::batch_args(*batch), k))
+    return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
+  const StepWs W = step_layout(batch, used);
+  if (ws_bytes < W.total || !ws) return fail(DSA_ERR_WORKSPACE, "step workspace too small");
+
+  const dsa::BatchArgs a = dsa::batch_args(*batch);
+  const int64_t per = (int64_t)batch->num_tokens * k;
+  void* mla_ws = static_cast<char*>(ws) + W.mla_off;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    const int64_t j = l / retention;
+    int32_t* latest = sel + j * per;
+    if (l % retention == 0) {
+      dsa_step_opts_t o{};
+      o.n_split = n_split;
+      if (mli && l > 0) {
+        o.mode = DSA_MODE_MLI;
+        o.attend_idx = sel + (j - 1) * per;
+      } else {
+        o.mode = DSA_MODE_FUSED;
+      }
+      rc = dsa_decode_step(batch, &L.ix, &L.mla, k, &o, latest, L.out, L.lse, ws, ws_bytes,
+                           stream_main, stream_aux);
+      if (rc) return rc;
+    } else {
+      // a layer without an indexer attends the latest indexer layer's selection
+      hipError_t e = dsa::launch_sparse_mla(a, L.mla.q, L.mla.kv_cache, latest, k,
+                                            L.mla.sm_scale, L.out, L.lse, used, mla_ws,
+                                            (hipStream_t)stream_main);
+      if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+    }
+  }
+  return DSA_OK;
+}
+
 size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n_split) {
   if (check_batch(batch) != DSA_OK || k < 1 || k > DSA_MAX_TOPK) return 0;
   const BatchArgs a = dsa::batch_args(*batch);

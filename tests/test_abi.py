@@ -132,6 +132,35 @@ def test_sparse_mla_paged_argument_checks(L):
                                          need - 1, None) == B.DSA_ERR_WORKSPACE
 
 
+def test_decode_layers_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    assert ctypes.sizeof(B.dsa_layer_t) == 80
+    assert B.dsa_layer_t.out.offset == 64 and B.dsa_layer_t.lse.offset == 72
+    full = B.dsa_layer_t(B.dsa_indexer_inputs_t(P, P, P, P, P), B.dsa_mla_inputs_t(P, P, 0.07), P,
+                         None)
+    bare = B.dsa_layer_t(B.dsa_indexer_inputs_t(), B.dsa_mla_inputs_t(P, P, 0.07), P, None)
+    need = L.dsa_workspace_size(B.DSA_OP_DECODE_STEP, ctypes.byref(b), 64, 0)
+
+    def call(layers, retention=2, mli=0, aux=None, ws=need):
+        arr = (B.dsa_layer_t * len(layers))(*layers)
+        return L.dsa_decode_layers(ctypes.byref(b), len(layers), arr, 64, retention, mli, 0, P, P,
+                                   ws, None, aux)
+
+    assert L.dsa_decode_layers(ctypes.byref(b), 0, None, 64, 1, 0, 0, P, P, need, None, None) == \
+        B.DSA_ERR_INVALID_ARG
+    assert call([full, bare], retention=0) == B.DSA_ERR_INVALID_ARG
+    assert call([full, bare], mli=2) == B.DSA_ERR_INVALID_ARG
+    assert call([full, bare], mli=1) == B.DSA_ERR_INVALID_ARG  # no second stream
+    assert call([full, bare, bare], retention=2) == B.DSA_ERR_INVALID_ARG  # layer 2 has no indexer
+    assert "indexer" in _err(L)
+    no_out = B.dsa_layer_t(B.dsa_indexer_inputs_t(), B.dsa_mla_inputs_t(P, P, 0.07), None, None)
+    assert call([full, no_out]) == B.DSA_ERR_INVALID_ARG
+    # layers without an indexer may leave its inputs NULL: validation passes
+    # and the call stops at the (too small) workspace, before any launch
+    assert call([full, bare, full, bare], retention=2, ws=need - 1) == B.DSA_ERR_WORKSPACE
+
+
 def test_sparse_mla_argument_checks(L):
     P = 0x1000
     b = _batch()
