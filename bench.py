@@ -350,6 +350,46 @@ def index_space_measure(b, d, iters=20):
     return res
 
 
+def short_measure(steps):
+    """The short-context form: 64 requests x 2 rows onto 2048 cached tokens
+    (every row keeps all its tokens).  The step selects without scanning and
+    attends densely; against it, the scan path the step would otherwise take
+    (indexer scores, top-k, sparse attention), same results."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    import synth
+    from synth.device import to_device
+    b = synth.make_batch([2] * 64, [2048] * 64, seed=83, paging="shuffled", heavy=16,
+                         pool_extra_pages=3)
+    d = to_device(b)
+    step = Step(b, d)
+    k = synth.TOPK
+    ld = 2048
+    scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
+    tk = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, d.meta, k)
+    mk = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, d.meta, k)
+    ws_t = torch.empty(tk, dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(max(mk, 1), dtype=torch.uint8, device="cuda")
+
+    def scan_path():
+        dsa.dsa_index_score(d.meta, d.q8, d.q_scale, d.w, d.k8[0], d.k_scale[0], scores, ld)
+        dsa.dsa_topk(d.meta, scores, ld, k, step.idx, ws_t, tk)
+        dsa.dsa_sparse_mla_decode(d.meta, d.q[0], d.kv[0], step.idx, k, synth.SM_SCALE, step.out,
+                                  step.lse, 0, ws_m, mk)
+
+    res = {"workload": "decode-b64-mtp1-ctx2048", "query_rows": b.T}
+    dense, scan = [], []
+    for _ in range(3):
+        dense.append(wall_ms(step, steps))
+        scan.append(wall_ms(scan_path, steps))
+    res["ms_dense_step"], res["ms_scan_path"] = min(dense), min(scan)
+    res["speedup"] = res["ms_scan_path"] / res["ms_dense_step"]
+    del step, d, scores, ws_t, ws_m
+    torch.cuda.empty_cache()
+    return res
+
+
 def mli_measure(steps):
     """Two-stream MLI step vs the same kernels back to back on one stream."""
     import numpy as np
@@ -501,6 +541,8 @@ def main():
         log(f"prefill {result['prefill']}")
         result["mli"] = mli_measure(max(5, args.steps // 2))
         log(f"mli {result['mli']}")
+        result["short_context"] = short_measure(max(5, args.steps // 2))
+        log(f"short context {result['short_context']}")
         result["cache_append"] = append_measure()
         log(f"cache append {result['cache_append']}")
         result["index_space"] = space

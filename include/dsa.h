@@ -197,6 +197,20 @@ int dsa_sparse_mla_decode_paged(const dsa_batch_t* batch, const uint16_t* q,
                                 float sm_scale, uint16_t* out, float* lse, int32_t n_split,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Dense absorbed-MLA decode: the attention of dsa_sparse_mla_decode over
+ * every visible position 0 .. v_t-1 of each row, with no index array -- the
+ * short-sequence fallback ("MTP and sparse attention: NSA and DSA": at short
+ * contexts sparse attention saves little, and the DeepSeek-V3.2 report runs
+ * short sequences densely).  With v_t <= k it equals dsa_sparse_mla_decode
+ * over the top-k's selection, bit for bit (the top-k then selects every
+ * position, in order); dsa_decode_step takes this form by itself when
+ * max_seqlen_k <= k and skips the indexer scan.
+ *  ws  >= dsa_workspace_size(DSA_OP_DENSE_MLA, batch, any k, n_split)
+ * Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED (max_seqlen_k > 131072). */
+int dsa_dense_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
+                         float sm_scale, uint16_t* out, float* lse, int32_t n_split, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Indexer inputs of one layer (device pointers, layouts as dsa_index_score). */
 typedef struct {
   const uint8_t* q8;
@@ -244,7 +258,10 @@ typedef struct {
   void* const* stage_events;
 } dsa_step_opts_t;
 
-/* One decode step of one layer: indexer scores, top-k, sparse MLA.
+/* One decode step of one layer: indexer scores, top-k, sparse MLA.  When
+ * max_seqlen_k <= k every row keeps all its visible tokens, so the step
+ * writes that selection without scanning and attends densely (same results
+ * as the scan would give).
  *  ix, mla   this layer's inputs
  *  k         tokens kept per row
  *  idx_out   int32 [T, k] out: the selection of ix (as dsa_topk)
@@ -294,7 +311,8 @@ int dsa_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_laye
 typedef enum {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA = 2,
-  DSA_OP_DECODE_STEP = 3
+  DSA_OP_DECODE_STEP = 3,
+  DSA_OP_DENSE_MLA = 4 /* k is not used */
 } dsa_op;
 
 /* Workspace bytes an op needs for this batch, k and n_split (0 = the

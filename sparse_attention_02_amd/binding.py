@@ -14,7 +14,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP = 1, 2, 3
+DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP, DSA_OP_DENSE_MLA = 1, 2, 3, 4
 DSA_MODE_FUSED, DSA_MODE_MLI = 0, 1
 DSA_STAGE_INDEX_SCORE, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_NUM_STAGES = 0, 1, 2, 3
 DSA_IDX_LOGICAL, DSA_IDX_PAGED, DSA_IDX_RAGGED = 0, 1, 2
@@ -22,7 +22,7 @@ PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 12
 
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
            "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
-           "dsa_decode_layers",
+           "dsa_decode_layers", "dsa_dense_mla_decode",
            "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
 
 
@@ -85,9 +85,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_decode_paged.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
         L.dsa_decode_layers.argtypes = [bp, i32, ctypes.POINTER(dsa_layer_t), i32, i32, i32, i32,
                                         vp, vp, sz, vp, vp]
+        L.dsa_dense_mla_decode.argtypes = [bp, vp, vp, f32, vp, vp, i32, vp, sz, vp]
         for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
                   "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
-                  "dsa_decode_layers"):
+                  "dsa_decode_layers", "dsa_dense_mla_decode"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
         L.dsa_workspace_size.restype = sz
@@ -183,6 +184,13 @@ def dsa_sparse_mla_decode_paged(batch: Batch, q, kv_cache, slots, k: int, sm_sca
                                              int(k), float(sm_scale), _ptr(out), _ptr(lse),
                                              int(n_split), _ptr(ws), int(ws_bytes),
                                              _stream(stream)))
+
+
+def dsa_dense_mla_decode(batch: Batch, q, kv_cache, sm_scale: float, out, lse, n_split: int, ws,
+                         ws_bytes: int, stream=None):
+    _check(lib().dsa_dense_mla_decode(batch.ref(), _ptr(q), _ptr(kv_cache), float(sm_scale),
+                                      _ptr(out), _ptr(lse), int(n_split), _ptr(ws), int(ws_bytes),
+                                      _stream(stream)))
 
 
 def dsa_sparse_mla_decode(batch: Batch, q, kv_cache, idx, k: int, sm_scale: float, out, lse,

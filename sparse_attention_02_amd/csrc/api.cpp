@@ -2,6 +2,7 @@
 // stream orchestration.  All arithmetic runs in the HIP kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <string>
 
@@ -200,6 +201,11 @@ size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n
     case DSA_OP_DECODE_STEP:
       if (resolve_splits(batch, k, n_split, &used) != DSA_OK) return 0;
       return step_layout(batch, used).total;
+    case DSA_OP_DENSE_MLA:
+      if (resolve_splits(batch, std::max(1, batch->max_seqlen_k), n_split, &used) != DSA_OK ||
+          used > dsa::kMaxSplits)
+        return 0;
+      return dsa::mla_ws_layout(a, used).total;
     default:
       return 0;
   }
@@ -265,23 +271,30 @@ int topk_common(const dsa_batch_t* batch, const float* scores, int64_t ld, int32
 
 int mla_common(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
                const int32_t* idx, int32_t k, float sm_scale, uint16_t* out, float* lse,
-               int32_t n_split, void* ws, size_t ws_bytes, void* stream, bool paged) {
+               int32_t n_split, void* ws, size_t ws_bytes, void* stream, int idx_mode) {
   g_err.clear();
   int rc = check_batch(batch);
   if (rc) return rc;
-  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  if (idx_mode == dsa::kMlaDense) {
+    k = std::max(1, batch->max_seqlen_k);  // the dense form attends every visible position
+  } else if (k < 1 || k > DSA_MAX_TOPK) {
+    return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  }
   int used = 1;
   rc = resolve_splits(batch, k, n_split, &used);
   if (rc) return rc;
+  if (used > dsa::kMaxSplits)
+    return fail(DSA_ERR_UNSUPPORTED, "dense attention covers at most 131072 tokens per row");
   if (batch->num_tokens == 0) return DSA_OK;
-  if (!q || !idx || !out || (!kv_cache && (batch->max_seqlen_k > 0 || paged)))
+  if (!q || !out || (!idx && idx_mode != dsa::kMlaDense) ||
+      (!kv_cache && (batch->max_seqlen_k > 0 || idx_mode == dsa::kMlaPaged)))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   const dsa::BatchArgs a = dsa::batch_args(*batch);
   const size_t need = dsa::mla_ws_layout(a, used).total;
   if (need > 0 && (ws_bytes < need || !ws))
     return fail(DSA_ERR_WORKSPACE, "attention workspace too small");
   hipError_t e = dsa::launch_sparse_mla(a, q, kv_cache, idx, k, sm_scale, out, lse, used, ws,
-                                        (hipStream_t)stream, paged);
+                                        (hipStream_t)stream, idx_mode);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA launch");
 }
 
@@ -302,7 +315,14 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uin
                           const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
                           float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream) {
   return mla_common(batch, q, kv_cache, idx, k, sm_scale, out, lse, n_split, ws, ws_bytes, stream,
-                    false);
+                    dsa::kMlaLogical);
+}
+
+int dsa_dense_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
+                         float sm_scale, uint16_t* out, float* lse, int32_t n_split, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return mla_common(batch, q, kv_cache, nullptr, 0, sm_scale, out, lse, n_split, ws, ws_bytes,
+                    stream, dsa::kMlaDense);
 }
 
 int dsa_sparse_mla_decode_paged(const dsa_batch_t* batch, const uint16_t* q,
@@ -310,7 +330,7 @@ int dsa_sparse_mla_decode_paged(const dsa_batch_t* batch, const uint16_t* q,
                                 float sm_scale, uint16_t* out, float* lse, int32_t n_split,
                                 void* ws, size_t ws_bytes, void* stream) {
   return mla_common(batch, q, kv_cache, slots, k, sm_scale, out, lse, n_split, ws, ws_bytes, stream,
-                    true);
+                    dsa::kMlaPaged);
 }
 
 int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
@@ -354,8 +374,23 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
     return hipEventRecord((hipEvent_t)opts->stage_events[2 * stage + end], s);
   };
 
+  // rows whose visible tokens all fit in k select every one of them: no
+  // scan is needed (the short-context dense form); the attention then takes
+  // the positions in order, exactly as it would from the top-k's output
+  const bool dense = batch->max_seqlen_k <= k;
   auto select = [&](hipStream_t s) -> int {
-    hipError_t e = dsa::launch_topk_zero(a, topk_ws, s);
+    hipError_t e;
+    if (dense) {
+      if ((e = mark(DSA_STAGE_INDEX_SCORE, 0, s)) != hipSuccess ||
+          (e = mark(DSA_STAGE_INDEX_SCORE, 1, s)) != hipSuccess ||
+          (e = mark(DSA_STAGE_TOPK, 0, s)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord");
+      e = dsa::launch_select_all(a, k, idx_out, s);
+      if (e != hipSuccess) return hip_fail(e, "select launch");
+      if ((e = mark(DSA_STAGE_TOPK, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      return DSA_OK;
+    }
+    e = dsa::launch_topk_zero(a, topk_ws, s);
     if (e != hipSuccess) return hip_fail(e, "top-k zero launch");
     if ((e = mark(DSA_STAGE_INDEX_SCORE, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
@@ -368,11 +403,11 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
     if ((e = mark(DSA_STAGE_TOPK, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return DSA_OK;
   };
-  auto attend = [&](const int32_t* sel) -> int {
+  auto attend = [&](const int32_t* sel, int idx_mode) -> int {
     hipError_t e = mark(DSA_STAGE_ATTENTION, 0, sm);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = dsa::launch_sparse_mla(a, mla->q, mla->kv_cache, sel, k, mla->sm_scale, out, lse, used,
-                               mla_ws, sm);
+                               mla_ws, sm, idx_mode);
     if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
     if ((e = mark(DSA_STAGE_ATTENTION, 1, sm)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return DSA_OK;
@@ -381,7 +416,7 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (!mli) {
     rc = select(sm);
     if (rc) return rc;
-    return attend(idx_out);
+    return attend(idx_out, dense ? dsa::kMlaDense : dsa::kMlaLogical);
   }
 
   // MLI: attention over the previous indexer layer's selection on the main
@@ -396,7 +431,7 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   rc = select(sa);
   if (rc) return rc;
-  rc = attend(opts->attend_idx);
+  rc = attend(opts->attend_idx, dsa::kMlaLogical);
   if (rc) return rc;
   e = hipEventRecord(ev_done, sa);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -71,9 +71,15 @@ bool topk_supported(const BatchArgs& b, int k);
 hipError_t launch_cache_append(const BatchArgs& b, const uint16_t* k_new, const uint16_t* kv_new,
                                uint8_t* k8, float* ks, uint16_t* kv, hipStream_t s);
 
-// paged: idx holds physical slots (DSA_IDX_PAGED) instead of logical positions
+// What the attention's idx holds: logical positions, physical slots, or
+// nothing (dense: every visible position among the first k, idx unused).
+enum MlaIndex { kMlaLogical = 0, kMlaPaged = 1, kMlaDense = 2 };
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
                              const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,
-                             int n_split, void* ws, hipStream_t s, bool paged = false);
+                             int n_split, void* ws, hipStream_t s, int idx_mode = kMlaLogical);
+
+// idx[t, j] = j for j < v_t (j < k), -1 after: the selection of a row whose
+// visible tokens all fit in k.
+hipError_t launch_select_all(const BatchArgs& b, int k, int32_t* idx, hipStream_t s);
 
 }  // namespace dsa

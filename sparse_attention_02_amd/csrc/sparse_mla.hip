@@ -120,7 +120,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
                        const int32_t* __restrict__ idx, int k, float scale_log2,
                        uint16_t* __restrict__ out, float* __restrict__ lse,
                        float* __restrict__ opart, float* __restrict__ lpart, int n_split, int chunk,
-                       int n_work, int per_xcd, bool paged) {
+                       int n_work, int per_xcd, int idx_mode) {
   __shared__ __attribute__((aligned(16))) unsigned char Ks0[kKsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ks1[kKsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ks2[kKsBytes];
@@ -153,14 +153,15 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int g = lane >> 4;
   const int head = wave * 16 + l16;
 
-  // position -> slot for the whole split (-1: skipped); with paged indices
-  // the entries are slots already and only their range is checked
+  // position -> slot for the whole split (-1: skipped); paged entries are
+  // slots already (only their range is checked); the dense form attends
+  // every visible position, the entry being the position itself
   const int64_t n_slots = (int64_t)b.num_pages * DSA_PAGE_SIZE;
   for (int i = tid; i < ntiles * kMlaTile; i += kThreads) {
     int slot = -1;
     if (i < ntok) {
-      const int s = idx[(int64_t)t * k + j0 + i];
-      if (paged) {
+      const int s = idx_mode == kMlaDense ? j0 + i : idx[(int64_t)t * k + j0 + i];
+      if (idx_mode == kMlaPaged) {
         if (s >= 0 && s < n_slots) slot = s;
       } else if (s >= 0 && s < v) {
         const int64_t sl = slot_of(b, bi, s);
@@ -491,7 +492,7 @@ int mla_splits_used(int k, int n_split) {
 
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
                              const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,
-                             int n_split, void* ws, hipStream_t s, bool paged) {
+                             int n_split, void* ws, hipStream_t s, int idx_mode) {
   if (b.T == 0) return hipSuccess;
   int chunk, used;
   split_shape(k, n_split, &chunk, &used);
@@ -501,7 +502,7 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
   if (used == 1) {
     hipLaunchKernelGGL((sparse_mla_kernel<false>), dim3(8 * per_xcd), dim3(kThreads), 0, s, b, q,
                        kv, idx, k, scale_log2, out, lse, (float*)nullptr, (float*)nullptr, 1,
-                       chunk, n_work, per_xcd, paged);
+                       chunk, n_work, per_xcd, idx_mode);
     return hipGetLastError();
   }
   const MlaWs L = mla_ws_layout(b, used);
@@ -510,7 +511,7 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
   float* lpart = reinterpret_cast<float*>(base + L.lpart_off);
   hipLaunchKernelGGL((sparse_mla_kernel<true>), dim3(8 * per_xcd), dim3(kThreads), 0, s, b, q, kv,
                      idx, k, scale_log2, out, lse, opart, lpart, used, chunk, n_work, per_xcd,
-                     paged);
+                     idx_mode);
   hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(b.T * DSA_MLA_HEADS)), dim3(128), 0, s,
                      opart, lpart, used, out, lse);
   return hipGetLastError();

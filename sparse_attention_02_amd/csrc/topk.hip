@@ -426,6 +426,14 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     out[i] = i < K ? index_in_space(b, bi, space, kv_off, sel[i]) : -1;
 }
 
+// the selection of rows whose visible tokens all fit in k: every position
+__global__ void select_all_kernel(BatchArgs b, int k, int32_t* __restrict__ idx) {
+  const int t = blockIdx.y;
+  const int v = row_len(b, t);
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < k; j += gridDim.x * blockDim.x)
+    idx[(int64_t)t * k + j] = j < v ? j : -1;
+}
+
 }  // namespace
 
 TopkWs topk_ws_layout(const BatchArgs& b) {
@@ -491,6 +499,13 @@ hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_select(b, scores, ld, k, idx, ws, s, space, kv_off);
+}
+
+hipError_t launch_select_all(const BatchArgs& b, int k, int32_t* idx, hipStream_t s) {
+  if (b.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_all_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)b.T), dim3(256), 0,
+                     s, b, k, idx);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -161,6 +161,21 @@ def test_decode_layers_argument_checks(L):
     assert call([full, bare, full, bare], retention=2, ws=need - 1) == B.DSA_ERR_WORKSPACE
 
 
+def test_dense_mla_argument_checks(L):
+    P = 0x1000
+    b = _batch()
+    need = L.dsa_workspace_size(B.DSA_OP_DENSE_MLA, ctypes.byref(b), 1, 4)
+    assert need >= 4 * 4 * 128 * 512 * 4  # 4 splits of 4 rows
+    assert L.dsa_dense_mla_decode(ctypes.byref(b), None, P, 0.1, P, None, 4, P, need, None) == \
+        B.DSA_ERR_INVALID_ARG
+    assert L.dsa_dense_mla_decode(ctypes.byref(b), P, P, 0.1, P, None, 4, P, need - 1, None) == \
+        B.DSA_ERR_WORKSPACE
+    long = _batch(max_seqlen_k=131073, max_pages=2049)
+    assert L.dsa_workspace_size(B.DSA_OP_DENSE_MLA, ctypes.byref(long), 1, 0) == 0
+    assert L.dsa_dense_mla_decode(ctypes.byref(long), P, P, 0.1, P, None, 0, P, 1 << 40, None) == \
+        B.DSA_ERR_UNSUPPORTED
+
+
 def test_sparse_mla_argument_checks(L):
     P = 0x1000
     b = _batch()
@@ -221,7 +236,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("DSA_MODE_FUSED", "DSA_MODE_MLI", "DSA_STAGE_INDEX_SCORE", "DSA_STAGE_TOPK",
                  "DSA_STAGE_ATTENTION", "DSA_NUM_STAGES", "DSA_OP_TOPK", "DSA_OP_SPARSE_MLA",
-                 "DSA_OP_DECODE_STEP", "DSA_IDX_LOGICAL", "DSA_IDX_PAGED", "DSA_IDX_RAGGED"):
+                 "DSA_OP_DECODE_STEP", "DSA_OP_DENSE_MLA", "DSA_IDX_LOGICAL", "DSA_IDX_PAGED",
+                 "DSA_IDX_RAGGED"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(B, name), name
 
