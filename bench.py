@@ -13,11 +13,15 @@ algorithmic bytes over the average of those per-launch durations.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extras]
   python bench.py --summarize-trace DIR            (rocprofv3 --kernel-trace --stats output)
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR   (two rocprofv3 --pmc runs)
+  python bench.py --summarize-mfma DIR     (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE)
 
---extras adds two more measurements to the line: the prefill-chunk form
-(4096 query rows on a 61440-token prefix: indexer FP8 MFMA utilisation) and
-the two-stream multi-layer-indexer step on a ragged 48-request batch
-(selection overlap of adjacent layers, time against the one-stream step).
+--extras adds more measurements to the line: the prefill-chunk form
+(4096 query rows on a 61440-token prefix: indexer FP8 MFMA utilisation), the
+two-stream multi-layer-indexer step on a ragged 48-request batch (selection
+overlap of adjacent layers, time against the one-stream step), the layer
+stack, the short-context form, cache appends, index spaces, the gathered
+bytes counted once per request, and the single-request step (1 row onto
+8192 tokens) warm and cold.  --prefill-only times just the prefill form.
 """
 from __future__ import annotations
 
@@ -186,7 +190,16 @@ def timed_steps(step, steps, warmup):
     torch.cuda.synchronize()
     stage_ms = [sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in sets) / steps
                 for i in range(dsa.DSA_NUM_STAGES)]
+    # device time of each step: from the event before its first stage to the
+    # one after its last
+    timed_steps.last_step_ms = [evs[0].elapsed_time(evs[-1]) for evs in sets]
     return ms_step, stage_ms
+
+
+def percentiles(xs):
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
+    return {"p10": float(p10), "p50": float(p50), "p90": float(p90), "n": len(xs)}
 
 
 def wall_ms(fn, iters, warmup=2):
@@ -257,6 +270,75 @@ def prefill_measure(steps):
     del step, d
     torch.cuda.empty_cache()
     return res
+
+
+def latency_measure(iters=50, flush_mib=512):
+    """The single-request decode step (1 row onto 8192 cached tokens): warm
+    (inputs in cache from the previous step) and cold (a write of flush_mib
+    MiB between steps evicts them); device time per step from HIP events."""
+    import torch
+
+    import synth
+    from synth.device import to_device
+    b = synth.make_workload(0)
+    d = to_device(b)
+    step = Step(b, d)
+    flush = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda")
+    res = {"workload": b.name, "query_rows": b.T}
+    for name, cold in (("warm", False), ("cold", True)):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for _ in range(3):
+            step()
+        for a, c in evs:
+            if cold:
+                flush.fill_(1.0)
+            a.record()
+            step()
+            c.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = percentiles([1e3 * a.elapsed_time(c) for a, c in evs])
+    del step, d, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def union_bytes(b, idx):
+    """The stricter attention byte count: each request's distinct selected
+    latent rows once (its query rows can share reads), instead of per row."""
+    import torch
+    cu = [int(x) for x in b.cu_seqlens_q]
+    total = 0
+    for r in range(b.B):
+        sel = idx[cu[r]:cu[r + 1]].reshape(-1)
+        total += int(torch.unique(sel[sel >= 0]).numel())
+    return total * 1152
+
+
+def summarize_mfma(d, simds=1024):
+    """MFMA busy share per kernel from one rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: busy cycles summed over the
+    SIMDs / (the kernel's active cycles x SIMDs), the MfmaUtil formula of
+    rocprofv3's derived counters.  GRBM_GUI_ACTIVE is reported per XCD and
+    summed here, so the per-XCD mean stands for its maximum."""
+    import collections
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    n_xcd = 8
+    for r in csv.DictReader(open(f)):
+        agg[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    print("| kernel | dispatches | MFMA busy cycles (sum over SIMDs) | active cycles per XCD | "
+          "MFMA busy % |\n|---|---|---|---|---|")
+    for k, v in agg.items():
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        act = v.get("GRBM_GUI_ACTIVE")
+        if not busy or not act or sum(busy) == 0:
+            continue
+        b_avg = sum(busy) / len(busy)
+        a_avg = sum(act) / len(act) / n_xcd
+        print(f"| {k} | {len(busy)} | {b_avg:.4g} | {a_avg:.4g} | {100 * b_avg / (a_avg * simds):.1f} |")
 
 
 # bytes one appended token moves: its bf16 key (256) and latent row (1152)
@@ -468,13 +550,18 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=128,
                     help="query rows the CPU oracle baseline covers (all 128 of the workload: about 10 s)")
     ap.add_argument("--extras", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill-chunk form (for counter runs) and print it")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mfma", metavar="DIR")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
+    if args.summarize_mfma:
+        return summarize_mfma(args.summarize_mfma)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DSA decode path here runs on a single "
               "MI355X (no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
@@ -488,6 +575,9 @@ def main():
     from synth.device import to_device
 
     dsa.lib()
+    if args.prefill_only:
+        print(json.dumps(prefill_measure(args.steps)), flush=True)
+        return
     t0 = time.perf_counter()
     b = synth.make_workload(DECODE_WORKLOAD)
     log(f"generated {b.name} in {time.perf_counter() - t0:.1f}s")
@@ -495,6 +585,7 @@ def main():
     torch.cuda.synchronize()
     step = Step(b, d)
     ms_step, (ms_idx, ms_topk, ms_attn) = timed_steps(step, args.steps, args.warmup)
+    step_dev = percentiles(timed_steps.last_step_ms)
     T = b.T
     work = accounting.batch_work(b.seqlens_k, b.n_q)
     idx_gbs = work["indexer_bytes"] / (ms_idx * 1e-3) / 1e9
@@ -505,6 +596,7 @@ def main():
         f"{ms_topk:.3f} ms | attention {ms_attn:.3f} ms {attn_gbs:.0f} GB/s | step "
         f"{step_gbs:.0f} GB/s")
     space = index_space_measure(b, d) if args.extras else None
+    union = union_bytes(b, step.idx) if args.extras else None
     del step, d
     torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth()
@@ -529,6 +621,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": work["bytes"], "achieved_gbs": step_gbs,
                      "frac": step_gbs / HBM_PEAK_GBS, "device_copy_gbs": copy_gbs},
         "stages_ms": {"index_score": ms_idx, "topk": ms_topk, "attention": ms_attn},
+        "step_device_ms": step_dev,
         "roofline": {"kernel": "index_score_page_kernel", "bound": "hbm", "achieved": idx_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": idx_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": work["indexer_bytes"]},
@@ -546,6 +639,10 @@ def main():
         result["cache_append"] = append_measure()
         log(f"cache append {result['cache_append']}")
         result["index_space"] = space
+        result["step_hbm"]["gathered_bytes_union"] = union
+        result["step_hbm"]["gathered_bytes_per_row"] = work["attention_gather_bytes"]
+        result["latency"] = latency_measure()
+        log(f"single-request latency {result['latency']}")
         log(f"top-k + attention, logical vs physical-slot indices {result['index_space']}")
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)

@@ -78,6 +78,7 @@ def batch_work(seqlens_k, n_q, k: int = TOPK, dv: int = LATENT, dim: int = LATEN
     attn_bytes = 0
     idx_flops = 0
     mla_flops = 0
+    gather = 0
     rows = 0
     for L, nq in zip(seqlens_k, n_q):
         L, nq = int(L), int(nq)
@@ -89,7 +90,9 @@ def batch_work(seqlens_k, n_q, k: int = TOPK, dv: int = LATENT, dim: int = LATEN
             idx_flops += v * indexer_pair_flops()
             mla_flops += K * mla_pair_flops(latent=dv, rope=dim - dv)
             attn_bytes += K * latent_bytes_per_token(dv, dim - dv)
+            gather += K * latent_bytes_per_token(dv, dim - dv)
     idx_bytes += rows * (IDX_HEADS * IDX_DIM + 4 + IDX_HEADS * 4)
     attn_bytes += rows * (MLA_HEADS * dim * 2 + MLA_HEADS * dv * 2 + MLA_HEADS * 4 + k * 4)
     return {"rows": rows, "indexer_bytes": idx_bytes, "attention_bytes": attn_bytes,
-            "bytes": idx_bytes + attn_bytes, "indexer_flops": idx_flops, "mla_flops": mla_flops}
+            "bytes": idx_bytes + attn_bytes, "indexer_flops": idx_flops, "mla_flops": mla_flops,
+            "attention_gather_bytes": gather}
