@@ -390,15 +390,21 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
       if ((e = mark(DSA_STAGE_TOPK, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
       return DSA_OK;
     }
-    e = dsa::launch_topk_zero(a, topk_ws, s);
-    if (e != hipSuccess) return hip_fail(e, "top-k zero launch");
+    // rows short enough for the one-pass top-k need no histogram from the
+    // scan (nor the zeroed workspace it accumulates into)
+    const bool rows = dsa::topk_rows_fit(a, scores, ld);
+    if (!rows) {
+      e = dsa::launch_topk_zero(a, topk_ws, s);
+      if (e != hipSuccess) return hip_fail(e, "top-k zero launch");
+    }
     if ((e = mark(DSA_STAGE_INDEX_SCORE, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
-                                ld, dsa::topk_hist1(a, topk_ws), s);
+                                ld, rows ? nullptr : dsa::topk_hist1(a, topk_ws), s);
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
     if ((e = mark(DSA_STAGE_INDEX_SCORE, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = mark(DSA_STAGE_TOPK, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = dsa::launch_topk_select(a, scores, ld, k, idx_out, topk_ws, s);
+    e = rows ? dsa::launch_topk_rows(a, scores, ld, k, idx_out, s)
+             : dsa::launch_topk_select(a, scores, ld, k, idx_out, topk_ws, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     if ((e = mark(DSA_STAGE_TOPK, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return DSA_OK;

@@ -66,6 +66,12 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
                               int32_t* idx, void* ws, hipStream_t s, int space = DSA_IDX_LOGICAL,
                               const int32_t* kv_off = nullptr);
 uint32_t* topk_hist1(const BatchArgs& b, void* ws);
+// Rows of at most 65536 positions with 16-byte aligned rows: one launch,
+// one work-group per row, no workspace and no histogram from the scan.
+bool topk_rows_fit(const BatchArgs& b, const float* scores, int64_t ld);
+hipError_t launch_topk_rows(const BatchArgs& b, const float* scores, int64_t ld, int k,
+                            int32_t* idx, hipStream_t s, int space = DSA_IDX_LOGICAL,
+                            const int32_t* kv_off = nullptr);
 bool topk_supported(const BatchArgs& b, int k);
 
 hipError_t launch_cache_append(const BatchArgs& b, const uint16_t* k_new, const uint16_t* kv_new,

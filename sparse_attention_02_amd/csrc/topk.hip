@@ -31,6 +31,7 @@ constexpr int kPerThread = kTopkSeg / kCollectThreads;  // 32 scores per thread
 constexpr int kFinalThreads = 1024;
 constexpr int kBitmapWords = 12288;  // 48 KB: rows up to 393216 positions
 constexpr int kSortCap = 4096;       // bitonic fallback (rows longer than the bitmap)
+constexpr int kCandStage = 6144;     // candidates the final pass stages in LDS (48 KB)
 
 // ctrl words per row
 constexpr int kCtrlB1 = 0;     // threshold bin (-1: every visible position selected)
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     int32_t* __restrict__ idx, const uint2* __restrict__ cand, int64_t cand_stride, int space,
     const int32_t* __restrict__ kv_off) {
   __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ uint2 lcand[kCandStage];
   __shared__ int32_t sel[kSortCap];
   __shared__ uint32_t h[kTopkBins];
   __shared__ uint32_t scan[kFinalThreads];
@@ -313,20 +315,61 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   int32_t* out = idx + (int64_t)t * k;
   const uint2* cl = cand + (int64_t)t * cand_stride;
   const int need = K - n_above;
+  const bool refine = need > 0 && nc > 0 && b1 >= 0;
+  const bool bitmap_form = v <= kBitmapWords * 32;
 
-  uint32_t tau = 0xffffffffu, pcut = 0u;  // nothing from the candidates by default
-  if (need > 0 && nc > 0 && b1 >= 0) {
-    // second digit (key bits 20..10) from the collect pass's histogram
+  // Everything the row needs from global memory is requested at once: the
+  // second-digit histogram, the candidates (staged in LDS when they fit) and
+  // the positions already selected as "above" (k <= 8192: at most 8 per
+  // thread), so the work below waits for one round trip instead of one per
+  // pass.
+  constexpr int kAbovePer = DSA_MAX_TOPK / kFinalThreads;
+  int32_t ab[kAbovePer];
+#pragma unroll
+  for (int j = 0; j < kAbovePer; ++j) {
+    const int i = threadIdx.x + j * kFinalThreads;
+    ab[j] = i < n_above ? out[i] : -1;
+  }
+  const bool staged = nc <= kCandStage;
+  if (refine) {
     for (int i = threadIdx.x; i < kTopkBins; i += kFinalThreads)
       h[i] = hist2[(int64_t)t * kTopkBins + i];
-    __syncthreads();
+    if (staged) {
+      for (int base = 0; base < nc; base += 8 * kFinalThreads) {
+        uint2 c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cl[min(base + (int)threadIdx.x + u * kFinalThreads, nc - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (base + (int)threadIdx.x + u * kFinalThreads < nc)
+            lcand[base + threadIdx.x + u * kFinalThreads] = c[u];
+      }
+    }
+  }
+  if (bitmap_form) {
+    for (int i = threadIdx.x; i < ((v + 31) >> 5); i += kFinalThreads) bitmap[i] = 0u;
+  }
+  __syncthreads();
+  // candidate i, from LDS or (more than kCandStage of them) from global memory
+  auto cget = [&](int i) { return staged ? lcand[i] : cl[i]; };
+  auto each_cand = [&](auto f) {
+    if (staged) {
+      for (int i = threadIdx.x; i < nc; i += kFinalThreads) f(lcand[i]);
+    } else {
+      for_each_cand(cl, nc, f);
+    }
+  };
+
+  uint32_t tau = 0xffffffffu, pcut = 0u;  // nothing from the candidates by default
+  if (refine) {
+    // second digit (key bits 20..10) from the collect pass's histogram
     find_cut(h, kTopkBins, (uint32_t)need, &s_bin, &s_above, scan);
     const int b2 = s_bin;
     const uint32_t need2 = (uint32_t)need - s_above;
     // third digit (bits 9..0) over the candidates in (b1, b2)
     for (int i = threadIdx.x; i < 1024; i += kFinalThreads) h[i] = 0u;
     __syncthreads();
-    for_each_cand(cl, nc, [&](uint2 c) {
+    each_cand([&](uint2 c) {
       if (((c.x >> 10) & (kTopkBins - 1)) == (uint32_t)b2) atomicAdd(&h[c.x & 1023u], 1u);
     });
     __syncthreads();
@@ -345,7 +388,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
       const uint32_t npos = radix_select(
           nc, need3,
           [&](int i, uint32_t* x) {
-            const uint2 c = cl[i];
+            const uint2 c = cget(i);
             *x = ~c.y;
             return c.x == t_;
           },
@@ -354,22 +397,20 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     }
   }
   auto picked = [&](uint2 c) { return c.x > tau || (c.x == tau && c.y <= pcut); };
+  const bool from_cand = tau != 0xffffffffu || pcut != 0u;
 
-  if (v <= kBitmapWords * 32) {
-    const int nwords = (v + 31) >> 5;
-    for (int i = threadIdx.x; i < nwords; i += kFinalThreads) bitmap[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n_above; i += kFinalThreads) {
-      const int s = out[i];
-      atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-    }
-    if (tau != 0xffffffffu || pcut != 0u) {
-      for_each_cand(cl, nc, [&](uint2 c) {
+  if (bitmap_form) {
+#pragma unroll
+    for (int j = 0; j < kAbovePer; ++j)
+      if (ab[j] >= 0) atomicOr(&bitmap[ab[j] >> 5], 1u << (ab[j] & 31));
+    if (from_cand) {
+      each_cand([&](uint2 c) {
         if (picked(c)) atomicOr(&bitmap[c.y >> 5], 1u << (c.y & 31));
       });
     }
     __syncthreads();
     // ascending compaction: thread i owns words [i*per, (i+1)*per)
+    const int nwords = (v + 31) >> 5;
     const int per = (nwords + kFinalThreads - 1) / kFinalThreads;
     const int w0 = threadIdx.x * per, w1 = min(nwords, w0 + per);
     uint32_t cnt = 0;
@@ -391,11 +432,13 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   }
 
   // long rows: gather into LDS and sort (K <= kSortCap)
-  for (int i = threadIdx.x; i < n_above; i += kFinalThreads) sel[i] = out[i];
+#pragma unroll
+  for (int j = 0; j < kAbovePer; ++j)
+    if (ab[j] >= 0) sel[threadIdx.x + j * kFinalThreads] = ab[j];
   if (threadIdx.x == 0) s_count = n_above;
   __syncthreads();
-  if (tau != 0xffffffffu || pcut != 0u) {
-    for_each_cand(cl, nc, [&](uint2 c) {
+  if (from_cand) {
+    each_cand([&](uint2 c) {
       if (picked(c)) {
         const int a = atomicAdd(&s_count, 1);
         if (a < kSortCap) sel[a] = (int32_t)c.y;
@@ -424,6 +467,210 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   }
   for (int i = threadIdx.x; i < k; i += kFinalThreads)
     out[i] = i < K ? index_in_space(b, bi, space, kv_off, sel[i]) : -1;
+}
+
+// ---- rows of at most 65536 positions: one work-group per row -------------
+//
+// The row's keys stay in registers (KPT per thread, read once with 16-byte
+// loads) and the three radix passes (11, 11, 10 bits) histogram them in LDS,
+// so the selection needs one read of the scores and no global atomics,
+// candidate lists or second launch.  Keys equal to the threshold are ranked
+// by position through an LDS bitmap (the lowest positions win), and the
+// selected positions leave in ascending order by a compaction of the bitmap.
+
+constexpr int kRowThreads = 1024;
+constexpr int kRowMax = 64 * kRowThreads;  // longest row: 64 keys per thread
+constexpr int kCopies = 8;                 // copies of the pass-1 histogram
+constexpr int kCopyStride = kTopkBins + 1;
+
+// find_cut for 1024 threads and 1024 or 2048 bins: the suffix sums run as
+// shuffles inside each wave plus one exchange of the 16 wave totals.
+__device__ void find_cut_1k(const uint32_t* h, int nbins, uint32_t need, int* bin,
+                            uint32_t* above, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per = nbins / kRowThreads;
+  const int lo = threadIdx.x * per;
+  uint32_t mine = 0;
+  for (int i = 0; i < per; ++i) mine += h[lo + i];
+  uint32_t inc = mine;  // inclusive suffix sum over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(inc, off);
+    if (lane + off < 64) inc += y;
+  }
+  if (lane == 0) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t run = inc - mine;  // bins above this thread's range
+  for (int w = wave + 1; w < kRowThreads / 64; ++w) run += wsum[w];
+  for (int i = lo + per - 1; i >= lo; --i) {
+    const uint32_t c = h[i];
+    if (run < need && run + c >= need) {
+      *bin = i;
+      *above = run;
+    }
+    run += c;
+  }
+  __syncthreads();
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
+    BatchArgs b, const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx,
+    int space, const int32_t* __restrict__ kv_off) {
+  constexpr int Q = KPT / 4;                // 16-byte groups per thread
+  constexpr int NW = KPT * kRowThreads / 32;  // bitmap words
+  // pass-1 histogram in kCopies copies (lane l counts into copy l % kCopies,
+  // the copies a bank apart): a row's keys crowd into the few first-digit
+  // bins of their binades, and same-bin increments from one instruction
+  // serialise unless spread over copies
+  __shared__ uint32_t hc[kCopies * kCopyStride];
+  __shared__ uint32_t h[kTopkBins];
+  __shared__ uint32_t bm[NW];   // selected positions
+  __shared__ uint32_t tie[NW];  // positions whose key equals the threshold
+  __shared__ uint32_t wsum[16];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const int t = blockIdx.x;
+  const int bi = row_request(b.cu, b.B, t);
+  const int v = row_visible(b, bi, t);
+  const int K = min(k, v);
+  const int tid = threadIdx.x;
+  int32_t* out = idx + (int64_t)t * k;
+  if (v <= k) {
+    // every visible position is selected
+    for (int i = tid; i < k; i += kRowThreads)
+      out[i] = i < v ? index_in_space(b, bi, space, kv_off, i) : -1;
+    return;
+  }
+
+  // group q of this thread: positions 4 tid + 4096 q + e, e < 4 (groups past
+  // the row re-read its last aligned group and are masked below)
+  const float* row = scores + (int64_t)t * ld;
+  const int last = (v - 1) & ~3;
+  v4f x[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    x[q] = *reinterpret_cast<const v4f*>(row + min(4 * tid + 4096 * q, last));
+  uint32_t key[Q][4];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[q][e] = float_key(x[q][e]);
+  auto valid = [&](int q, int e) { return 4 * tid + 4096 * q + e < v; };
+
+  // pass 1: bits 31..21
+  for (int i = tid; i < kCopies * kCopyStride; i += kRowThreads) hc[i] = 0u;
+  __syncthreads();
+  {
+    uint32_t* mine = hc + (tid % kCopies) * kCopyStride;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(q, e)) atomicAdd(&mine[key[q][e] >> 21], 1u);
+  }
+  __syncthreads();
+  for (int i = tid; i < kTopkBins; i += kRowThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) c += hc[j * kCopyStride + i];
+    h[i] = c;
+  }
+  __syncthreads();
+  if (tid == 0) s_bin = 0;
+  find_cut_1k(h, kTopkBins, (uint32_t)K, &s_bin, &s_above, wsum);
+  const uint32_t b1 = (uint32_t)s_bin;
+  uint32_t need = (uint32_t)K - s_above;
+  __syncthreads();
+  // pass 2: bits 20..10 of the keys in bin b1
+  for (int i = tid; i < kTopkBins; i += kRowThreads) h[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (valid(q, e) && (key[q][e] >> 21) == b1) atomicAdd(&h[(key[q][e] >> 10) & 2047u], 1u);
+  __syncthreads();
+  if (tid == 0) s_bin = 0;
+  find_cut_1k(h, kTopkBins, need, &s_bin, &s_above, wsum);
+  const uint32_t p2 = (b1 << 11) | (uint32_t)s_bin;
+  need -= s_above;
+  __syncthreads();
+  // pass 3: bits 9..0 of the keys whose top 22 bits are p2
+  for (int i = tid; i < 1024; i += kRowThreads) h[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (valid(q, e) && (key[q][e] >> 10) == p2) atomicAdd(&h[key[q][e] & 1023u], 1u);
+  __syncthreads();
+  if (tid == 0) s_bin = 0;
+  find_cut_1k(h, 1024, need, &s_bin, &s_above, wsum);
+  const uint32_t tau = (p2 << 10) | (uint32_t)s_bin;
+  const uint32_t need3 = need - s_above;  // keys equal to tau to keep (>= 1)
+  const uint32_t cnt_eq = h[s_bin];
+
+  // keys above tau, and keys equal to it, as bitmaps over the positions
+  // (the 4 positions of a group share a word)
+  for (int i = tid; i < NW; i += kRowThreads) {
+    bm[i] = 0u;
+    tie[i] = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!valid(q, e)) continue;
+      if (key[q][e] > tau) gt |= 1u << e;
+      else if (key[q][e] == tau) eq |= 1u << e;
+    }
+    const int word = (tid >> 3) + 128 * q;
+    const int sh = 4 * (tid & 7);
+    if (gt) atomicOr(&bm[word], gt << sh);
+    if (eq) atomicOr(&tie[word], eq << sh);
+  }
+  __syncthreads();
+  // thread i owns words [i*per, (i+1)*per)
+  constexpr int per = (NW + kRowThreads - 1) / kRowThreads;
+  const int w0 = min(NW, tid * per), w1 = min(NW, w0 + per);
+  if (need3 < cnt_eq) {
+    // the need3 lowest tie positions: ranks from a prefix sum in word order
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(tie[w]);
+    uint32_t tot;
+    uint32_t at = block_exclusive_sum(cnt, wsum, &tot);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t m = tie[w], keep = 0;
+      while (m) {
+        const uint32_t bit = m & (0u - m);
+        m ^= bit;
+        if (at < need3) keep |= bit;
+        ++at;
+      }
+      bm[w] |= keep;
+    }
+  } else {
+    for (int w = w0; w < w1; ++w) bm[w] |= tie[w];
+  }
+  __syncthreads();
+  // ascending compaction
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  uint32_t total;
+  uint32_t at = block_exclusive_sum(cnt, wsum, &total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bm[w];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      if (at < (uint32_t)K) out[at] = index_in_space(b, bi, space, kv_off, (w << 5) + bit);
+      ++at;
+    }
+  }
+  for (int i = K + tid; i < k; i += kRowThreads) out[i] = -1;
 }
 
 // the selection of rows whose visible tokens all fit in k: every position
@@ -491,6 +738,7 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
 hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int k, int32_t* idx,
                        void* ws, hipStream_t s, int space, const int32_t* kv_off) {
   if (b.T == 0) return hipSuccess;
+  if (topk_rows_fit(b, scores, ld)) return launch_topk_rows(b, scores, ld, k, idx, s, space, kv_off);
   hipError_t e = launch_topk_zero(b, ws, s);
   if (e != hipSuccess) return e;
   const int segs = std::max(1, (b.max_seqlen_k + kTopkSeg - 1) / kTopkSeg);
@@ -499,6 +747,24 @@ hipError_t launch_topk(const BatchArgs& b, const float* scores, int64_t ld, int 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_select(b, scores, ld, k, idx, ws, s, space, kv_off);
+}
+
+bool topk_rows_fit(const BatchArgs& b, const float* scores, int64_t ld) {
+  return b.max_seqlen_k <= kRowMax && (reinterpret_cast<uintptr_t>(scores) & 15) == 0 &&
+         ld % 4 == 0;
+}
+
+hipError_t launch_topk_rows(const BatchArgs& b, const float* scores, int64_t ld, int k,
+                            int32_t* idx, hipStream_t s, int space, const int32_t* kv_off) {
+  if (b.T == 0) return hipSuccess;
+  const dim3 grid(b.T), block(kRowThreads);
+  if (b.max_seqlen_k <= 8 * kRowThreads)
+    hipLaunchKernelGGL(topk_row_kernel<8>, grid, block, 0, s, b, scores, ld, k, idx, space, kv_off);
+  else if (b.max_seqlen_k <= 32 * kRowThreads)
+    hipLaunchKernelGGL(topk_row_kernel<32>, grid, block, 0, s, b, scores, ld, k, idx, space, kv_off);
+  else
+    hipLaunchKernelGGL(topk_row_kernel<64>, grid, block, 0, s, b, scores, ld, k, idx, space, kv_off);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_all(const BatchArgs& b, int k, int32_t* idx, hipStream_t s) {

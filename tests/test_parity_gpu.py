@@ -154,6 +154,49 @@ def test_topk_adversarial_scores(pattern):
             assert (g[i, K_:] == -1).all()
 
 
+def _meta(L, n_q=None):
+    """Batch metadata only (identity page table): enough for the top-k."""
+    n_q = n_q or [1] * len(L)
+    cu = np.concatenate([[0], np.cumsum(n_q)]).astype(np.int32)
+    mx = max(L)
+    pages = max(1, -(-mx // 64))
+    pt = np.tile(np.arange(pages, dtype=np.int32), (len(L), 1))
+    dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    return dsa.Batch(dev(cu), dev(np.asarray(L, np.int32)), dev(pt), pages, max(n_q), mx)
+
+
+@pytest.mark.parametrize("L", [[8192, 100], [8193, 40], [32768, 5000], [32769], [65536, 2049],
+                               [65537, 3000]])
+@pytest.mark.parametrize("k", [1, 2048, 8192])
+def test_topk_one_pass_and_multi_pass_agree(L, k):
+    """Rows of at most 65536 positions whose scores are 16-byte aligned with
+    ld % 4 == 0 take the one-pass kernel (keys held in registers); an odd ld
+    sends the same scores through the histogram, collect and final kernels.
+    Both selections equal the oracle's on these float32 scores (rounded to
+    0.01 so that many keys tie at the threshold), in ascending order."""
+    rng = np.random.default_rng(sum(L) + k)
+    meta = _meta(L)
+    T, mx = len(L), max(L)
+    s = np.round(rng.normal(size=(T, mx + 8)), 2).astype(np.float32)
+    vis = [min(x, mx) for x in L]
+    sel, _, _, Ks = O.topk(s.astype(np.float64), vis, k, band=0.0)
+    ws_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, meta, k)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    got = []
+    for ld in (mx + (-mx) % 4, mx + (-mx) % 4 + 1):
+        x = torch.from_numpy(np.ascontiguousarray(s[:, :ld])).cuda()
+        idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk(meta, x, ld, k, idx, ws, ws_bytes)
+        sync()
+        g = idx.cpu().numpy()
+        for i in range(T):
+            K_ = int(Ks[i])
+            assert g[i, :K_].tolist() == sorted(sel[i, :K_].tolist()), (ld, i)
+            assert (g[i, K_:] == -1).all()
+        got.append(g)
+    assert np.array_equal(got[0], got[1])
+
+
 @pytest.mark.parametrize("ci", range(len(SMALL)))
 def test_selection_end_to_end_small(ci):
     b = _small(SMALL[ci], 400 + ci)
