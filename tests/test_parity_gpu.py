@@ -166,18 +166,24 @@ def _meta(L, n_q=None):
 
 
 @pytest.mark.parametrize("L", [[8192, 100], [8193, 40], [32768, 5000], [32769], [65536, 2049],
-                               [65537, 3000]])
+                               [65537, 3000], [131072, 70001], [200003]])
 @pytest.mark.parametrize("k", [1, 2048, 8192])
-def test_topk_one_pass_and_multi_pass_agree(L, k):
-    """Rows of at most 65536 positions whose scores are 16-byte aligned with
-    ld % 4 == 0 take the one-pass kernel (keys held in registers); an odd ld
-    sends the same scores through the histogram, collect and final kernels.
-    Both selections equal the oracle's on these float32 scores (rounded to
-    0.01 so that many keys tie at the threshold), in ascending order."""
+@pytest.mark.parametrize("pattern", ["rounded", "few_values"])
+def test_topk_one_pass_and_multi_pass_agree(L, k, pattern):
+    """With scores 16-byte aligned and ld % 4 == 0, rows of at most 65536
+    positions take the one-pass kernel (keys held in registers); longer rows,
+    or an odd ld, go through the histogram, collect and final kernels (with
+    few distinct values the final pass's candidates overflow its LDS stage
+    and are read from the workspace list).  Both selections equal the
+    oracle's on these float32 scores (rounded to 0.01, or 5 distinct values,
+    so that many keys tie at the threshold), in ascending order."""
     rng = np.random.default_rng(sum(L) + k)
     meta = _meta(L)
     T, mx = len(L), max(L)
-    s = np.round(rng.normal(size=(T, mx + 8)), 2).astype(np.float32)
+    if pattern == "rounded":
+        s = np.round(rng.normal(size=(T, mx + 8)), 2).astype(np.float32)
+    else:
+        s = rng.integers(0, 5, (T, mx + 8)).astype(np.float32)
     vis = [min(x, mx) for x in L]
     sel, _, _, Ks = O.topk(s.astype(np.float64), vis, k, band=0.0)
     ws_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, meta, k)
