@@ -399,7 +399,7 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
     }
     if ((e = mark(DSA_STAGE_INDEX_SCORE, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = dsa::launch_index_score(a, ix->q8, ix->q_scale, ix->w, ix->k8_cache, ix->k_scale, scores,
-                                ld, rows ? nullptr : dsa::topk_hist1(a, topk_ws), s);
+                                ld, rows ? nullptr : dsa::topk_hist1(a, topk_ws), s, mli);
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
     if ((e = mark(DSA_STAGE_INDEX_SCORE, 1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = mark(DSA_STAGE_TOPK, 0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");

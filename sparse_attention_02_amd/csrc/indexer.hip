@@ -29,7 +29,10 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 16;  // pages per work-group of the row-group form
 #ifndef DSA_SCAN_TARGET_WGS
-#define DSA_SCAN_TARGET_WGS 2048
+#define DSA_SCAN_TARGET_WGS 1024
+#endif
+#ifndef DSA_SCAN_SHARED_TARGET_WGS
+#define DSA_SCAN_SHARED_TARGET_WGS 2048
 #endif
 #ifndef DSA_SCAN_NPF1
 #define DSA_SCAN_NPF1 2
@@ -41,9 +44,16 @@ constexpr int kScanTargetWGs = DSA_SCAN_TARGET_WGS;
 constexpr int kScanNPF1 = DSA_SCAN_NPF1;
 constexpr int kScanNPF2 = DSA_SCAN_NPF2;
 #ifndef DSA_SCAN_STAGE_PAGES
-#define DSA_SCAN_STAGE_PAGES 64
+#define DSA_SCAN_STAGE_PAGES 128
 #endif
 constexpr int kStagePages = DSA_SCAN_STAGE_PAGES;  // most pages per work-group
+// beside another kernel (the attention of multi-layer-indexer mode) the scan
+// uses work-groups of at most 64 pages and half the LDS: finer-grained
+// work-groups free CUs for the other kernel sooner (two streams over the
+// 48-request ragged batch: 0.266 ms with 64-page work-groups, 0.289 ms with
+// 128, against 0.31 ms on one stream)
+constexpr int kSharedStagePages = 64;
+constexpr int kSharedTargetWGs = DSA_SCAN_SHARED_TARGET_WGS;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -246,7 +256,7 @@ __device__ __forceinline__ float reduce_scatter4(const float p[4]) {
   return __uint_as_float(d[0]) + __uint_as_float(d[1]);
 }
 
-template <int RG, int NPF, bool HIST>
+template <int RG, int NPF, bool HIST, int STAGE>
 __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
     BatchArgs b, const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
     uint32_t* __restrict__ hist, int chunk_pages) {
   __shared__ uint32_t lh[HIST ? RG * kTopkBins : 1];
   // the work-group's scores, written out in one burst at the end
-  __shared__ float lsc[RG][kStagePages * DSA_PAGE_SIZE];
+  __shared__ float lsc[RG][STAGE * DSA_PAGE_SIZE];
   const int chunk = blockIdx.x;
   const int bi = blockIdx.y;
   const int c0 = b.cu[bi];
@@ -418,39 +428,54 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
   }
 }
 
-template <int RG, int NPF>
+template <int RG, int NPF, int STAGE>
 hipError_t launch_page(int chunk_pages, int chunks, hipStream_t s, const BatchArgs& b,
                        const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
                        const float* k_scale, float* scores, int64_t ld, uint32_t* hist) {
   const dim3 grid(chunks, b.B);
   if (hist)
-    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, true>), grid, dim3(kThreads), 0, s, b,
-                       q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
+    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, true, STAGE>), grid, dim3(kThreads), 0,
+                       s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
   else
-    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, false>), grid, dim3(kThreads), 0, s, b,
-                       q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
+    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, false, STAGE>), grid, dim3(kThreads), 0,
+                       s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
   return hipGetLastError();
+}
+
+template <int RG, int NPF>
+hipError_t launch_page_sized(bool shared, int total_pages, hipStream_t s, const BatchArgs& b,
+                             const uint8_t* q8, const float* q_scale, const float* w,
+                             const uint8_t* k8, const float* k_scale, float* scores, int64_t ld,
+                             uint32_t* hist) {
+  // pages per work-group: about the target number of work-groups over the
+  // batch (sized for its longest request), at most STAGE pages (<= 64 per wave)
+  const int stage = shared ? kSharedStagePages : kStagePages;
+  const int target = shared ? kSharedTargetWGs : kScanTargetWGs;
+  const int64_t all = (int64_t)total_pages * b.B;
+  int cp = (int)std::min<int64_t>(stage, (all + target - 1) / target);
+  cp = std::max(kPageWaves, (cp + kPageWaves - 1) / kPageWaves * kPageWaves);
+  const int chunks = (total_pages + cp - 1) / cp;
+  if (shared)
+    return launch_page<RG, NPF, kSharedStagePages>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale,
+                                                   scores, ld, hist);
+  return launch_page<RG, NPF, kStagePages>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores,
+                                           ld, hist);
 }
 
 }  // namespace
 
 hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float* q_scale,
                               const float* w, const uint8_t* k8, const float* k_scale,
-                              float* scores, int64_t ld, uint32_t* hist, hipStream_t s) {
+                              float* scores, int64_t ld, uint32_t* hist, hipStream_t s,
+                              bool shared) {
   if (b.B == 0 || b.T == 0 || b.max_seqlen_k == 0) return hipSuccess;
   const int total_pages = (b.max_seqlen_k + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE;
   if (b.max_q <= 2) {
-    // pages per work-group: about kScanTargetWGs work-groups over the batch
-    // (sized for its longest request), at most 64 pages per wave
-    const int64_t all = (int64_t)total_pages * b.B;
-    int cp = (int)std::min<int64_t>(kStagePages, (all + kScanTargetWGs - 1) / kScanTargetWGs);
-    cp = std::max(kPageWaves, (cp + kPageWaves - 1) / kPageWaves * kPageWaves);
-    const int chunks = (total_pages + cp - 1) / cp;
     if (b.max_q <= 1)
-      return launch_page<1, kScanNPF1>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores, ld,
-                                       hist);
-    return launch_page<2, kScanNPF2>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores, ld,
-                                     hist);
+      return launch_page_sized<1, kScanNPF1>(shared, total_pages, s, b, q8, q_scale, w, k8,
+                                             k_scale, scores, ld, hist);
+    return launch_page_sized<2, kScanNPF2>(shared, total_pages, s, b, q8, q_scale, w, k8, k_scale,
+                                           scores, ld, hist);
   }
   const int groups = (b.max_q + 3) / 4;
   const int chunks = (total_pages + kChunk - 1) / kChunk;

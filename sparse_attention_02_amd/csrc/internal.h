@@ -51,9 +51,12 @@ int mla_splits_used(int k, int n_split);
 
 // hist (may be NULL): per-row histogram of the top 11 bits of each score's
 // order-preserving key, [T][kTopkBins], accumulated with atomics.
+// shared: the scan runs beside another kernel (multi-layer-indexer mode) and
+// uses smaller work-groups.
 hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float* q_scale,
                               const float* w, const uint8_t* k8, const float* k_scale,
-                              float* scores, int64_t ld, uint32_t* hist, hipStream_t s);
+                              float* scores, int64_t ld, uint32_t* hist, hipStream_t s,
+                              bool shared = false);
 
 // Whole top-k: zero, histogram, threshold, collect, final.
 // space: DSA_IDX_LOGICAL / PAGED / RAGGED (kv_off [B] for RAGGED, else unused)
