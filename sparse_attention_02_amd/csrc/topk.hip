@@ -81,26 +81,30 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(BatchArgs b,
 }
 
 // Largest bin `bin` of h[0..nbins) with sum_{b > bin} h[b] < need <=
-// sum_{b >= bin} h[b]; *above = sum_{b > bin} h[b].  Block-wide; need >= 1
-// and sum h >= need.  `scan` is LDS scratch of blockDim.x words.
+// sum_{b >= bin} h[b]; *above = sum_{b > bin} h[b].  Block-wide (blockDim.x a
+// multiple of 64, at most 1024); need >= 1 and sum h >= need, else *bin is
+// left as it was.  Each thread sums a run of bins, the suffix sums run as
+// shuffles inside each wave plus one exchange of the wave totals through
+// `scan` (at least 16 words of LDS): two barriers per call.
 __device__ void find_cut(const uint32_t* h, int nbins, uint32_t need, int* bin, uint32_t* above,
                          uint32_t* scan) {
   const int nt = blockDim.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = nt >> 6;
   const int per = (nbins + nt - 1) / nt;
-  const int lo = threadIdx.x * per;
+  const int lo = min(nbins, (int)threadIdx.x * per);
   const int hi = min(nbins, lo + per);
   uint32_t mine = 0;
   for (int i = lo; i < hi; ++i) mine += h[i];
-  scan[threadIdx.x] = mine;
-  __syncthreads();
-  // inclusive suffix sum over threads (Hillis-Steele)
-  for (int off = 1; off < nt; off <<= 1) {
-    uint32_t add = threadIdx.x + off < nt ? scan[threadIdx.x + off] : 0u;
-    __syncthreads();
-    scan[threadIdx.x] += add;
-    __syncthreads();
+  uint32_t inc = mine;  // inclusive suffix sum over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(inc, off);
+    if (lane + off < 64) inc += y;
   }
-  uint32_t run = scan[threadIdx.x] - mine;  // sum of bins above this thread's range
+  if (lane == 0) scan[wave] = inc;
+  __syncthreads();
+  uint32_t run = inc - mine;  // sum of bins above this thread's range
+  for (int w = wave + 1; w < nw; ++w) run += scan[w];
   for (int i = hi - 1; i >= lo; --i) {
     const uint32_t c = h[i];
     if (run < need && run + c >= need) {
@@ -483,36 +487,6 @@ constexpr int kRowMax = 64 * kRowThreads;  // longest row: 64 keys per thread
 constexpr int kCopies = 8;                 // copies of the pass-1 histogram
 constexpr int kCopyStride = kTopkBins + 1;
 
-// find_cut for 1024 threads and 1024 or 2048 bins: the suffix sums run as
-// shuffles inside each wave plus one exchange of the 16 wave totals.
-__device__ void find_cut_1k(const uint32_t* h, int nbins, uint32_t need, int* bin,
-                            uint32_t* above, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int per = nbins / kRowThreads;
-  const int lo = threadIdx.x * per;
-  uint32_t mine = 0;
-  for (int i = 0; i < per; ++i) mine += h[lo + i];
-  uint32_t inc = mine;  // inclusive suffix sum over the wave's lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(inc, off);
-    if (lane + off < 64) inc += y;
-  }
-  if (lane == 0) wsum[wave] = inc;
-  __syncthreads();
-  uint32_t run = inc - mine;  // bins above this thread's range
-  for (int w = wave + 1; w < kRowThreads / 64; ++w) run += wsum[w];
-  for (int i = lo + per - 1; i >= lo; --i) {
-    const uint32_t c = h[i];
-    if (run < need && run + c >= need) {
-      *bin = i;
-      *above = run;
-    }
-    run += c;
-  }
-  __syncthreads();
-}
-
 template <int KPT>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     BatchArgs b, const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx,
@@ -578,7 +552,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   }
   __syncthreads();
   if (tid == 0) s_bin = 0;
-  find_cut_1k(h, kTopkBins, (uint32_t)K, &s_bin, &s_above, wsum);
+  find_cut(h, kTopkBins, (uint32_t)K, &s_bin, &s_above, wsum);
   const uint32_t b1 = (uint32_t)s_bin;
   uint32_t need = (uint32_t)K - s_above;
   __syncthreads();
@@ -592,7 +566,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
       if (valid(q, e) && (key[q][e] >> 21) == b1) atomicAdd(&h[(key[q][e] >> 10) & 2047u], 1u);
   __syncthreads();
   if (tid == 0) s_bin = 0;
-  find_cut_1k(h, kTopkBins, need, &s_bin, &s_above, wsum);
+  find_cut(h, kTopkBins, need, &s_bin, &s_above, wsum);
   const uint32_t p2 = (b1 << 11) | (uint32_t)s_bin;
   need -= s_above;
   __syncthreads();
@@ -606,7 +580,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
       if (valid(q, e) && (key[q][e] >> 10) == p2) atomicAdd(&h[key[q][e] & 1023u], 1u);
   __syncthreads();
   if (tid == 0) s_bin = 0;
-  find_cut_1k(h, 1024, need, &s_bin, &s_above, wsum);
+  find_cut(h, 1024, need, &s_bin, &s_above, wsum);
   const uint32_t tau = (p2 << 10) | (uint32_t)s_bin;
   const uint32_t need3 = need - s_above;  // keys equal to tau to keep (>= 1)
   const uint32_t cnt_eq = h[s_bin];
