@@ -204,9 +204,12 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   for (int j = 0; j < kPerThread; ++j)
     if (em & (1u << j)) atomicAdd(&h2[(key[j] >> 10) & (kTopkBins - 1)], 1u);
 
-  uint32_t tot_a, tot_e;
-  const uint32_t ex_a = block_exclusive_sum(__popc(am), wsum, &tot_a);
-  const uint32_t ex_e = block_exclusive_sum(__popc(em), wsum, &tot_e);
+  // both counts in one scan: at most 8192 per work-group, so 16 bits each
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_sum(((uint32_t)__popc(am) << 16) | (uint32_t)__popc(em),
+                                          wsum, &tot);
+  const uint32_t ex_a = ex >> 16, ex_e = ex & 0xffffu;
+  const uint32_t tot_a = tot >> 16, tot_e = tot & 0xffffu;
   if (threadIdx.x == 0) {
     s_base[0] = tot_a ? atomicAdd(&ctrl[t * kCtrlWords + kCtrlAbove], (int)tot_a) : 0;
     s_base[1] = tot_e ? atomicAdd(&ctrl[t * kCtrlWords + kCtrlCand], (int)tot_e) : 0;
