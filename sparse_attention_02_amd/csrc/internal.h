@@ -40,7 +40,7 @@ struct TopkWs {
 TopkWs topk_ws_layout(const BatchArgs& b);
 
 struct MlaWs {
-  size_t opart_off, lpart_off, total;
+  size_t opart_off, spart_off, lpart_off, total;
 };
 MlaWs mla_ws_layout(const BatchArgs& b, int n_split);
 

@@ -29,6 +29,9 @@
 //            token-major tile through transposing LDS reads
 //            (ds_read_b64_tr_b16: four tokens of one dim per lane), in the
 //            token order in which the S^T accumulator holds P.
+// With several splits per row each writes its normalised partial output in
+// fp16, scaled per (head, 64-dim slice) by a power of two, plus the slice
+// scales and its lse, and a merge kernel combines them.
 // The loop is software-pipelined: step i runs the value product of tile i
 // and the scores of tile i+1 while tile i+2 streams in, with one barrier per
 // step.  Operand reads run ahead of the products that use them (two k-steps
@@ -114,12 +117,37 @@ struct Stage {
   uint8_t* raised;
 };
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// two floats as fp16 (round to nearest even) in one word, the first low
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const h2v v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(h2v, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(h2v, w)[1];
+}
+
+// power of two s with m * s in [2^14, 2^15) for a finite m > 0 (1 otherwise,
+// and clamped to the normal range): fp16 values of magnitude up to m keep 11
+// significant bits and stay far from the fp16 maximum
+__device__ __forceinline__ float half_scale(float m) {
+  if (!(m > 0.f) || !(m < INFINITY)) return 1.f;
+  const int e = (int)((__float_as_uint(m) >> 23) & 255u) - 127;  // floor(log2 m) for normal m
+  const int k = min(127, max(-126, 14 - e));
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
 template <bool SPLIT>
 __global__ __launch_bounds__(kThreads)
 void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                        const int32_t* __restrict__ idx, int k, float scale_log2,
                        uint16_t* __restrict__ out, float* __restrict__ lse,
-                       float* __restrict__ opart, float* __restrict__ lpart, int n_split, int chunk,
+                       uint16_t* __restrict__ opart, float* __restrict__ spart,
+                       float* __restrict__ lpart, int n_split, int chunk,
                        int n_work, int per_xcd, int idx_mode) {
   __shared__ __attribute__((aligned(16))) unsigned char Ks0[kKsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ks1[kKsBytes];
@@ -396,14 +424,35 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
             make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
       }
     } else {
-      float* o = opart + (((int64_t)t * n_split + split) * DSA_MLA_HEADS + h) * DSA_MLA_DV + d_base +
-                 4 * g;
+      // the split's partial in fp16, scaled per (head, this wave's 64 dims)
+      // by a power of two that puts its largest magnitude in [2^14, 2^15):
+      // 11 significant bits, against 8 for the bf16 output
+      float mx = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[db][hb][r]));
+      {  // max over the four 16-lane rows, which hold the head's other dims
+        const v2u x = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+        mx = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+        const v2u y = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+        mx = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+      }
+      const float sc = half_scale(mx * inv);
+      uint16_t* o = opart + (((int64_t)t * n_split + split) * DSA_MLA_HEADS + h) * DSA_MLA_DV +
+                    d_base + 4 * g;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const v4f x = acc[db][hb];
-        *reinterpret_cast<float4*>(o + 16 * db) =
-            make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+        const float f = inv * sc;
+        *reinterpret_cast<uint2*>(o + 16 * db) =
+            make_uint2(pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f));
       }
+      if (g == 0)
+        spart[(((int64_t)t * n_split + split) * (kThreads / 64) + wave) * DSA_MLA_HEADS + h] =
+            1.f / sc;
     }
   }
   if (g == 0) {
@@ -417,7 +466,8 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
 
 // out(t,h) = sum_j e^{lse_j - lse*} O_j / sum_j e^{lse_j - lse*},
 // lse(t,h) = lse* + ln sum_j e^{lse_j - lse*}, lse* = max_j lse_j.
-__global__ __launch_bounds__(128) void mla_merge_kernel(const float* __restrict__ opart,
+__global__ __launch_bounds__(128) void mla_merge_kernel(const uint16_t* __restrict__ opart,
+                                                        const float* __restrict__ spart,
                                                         const float* __restrict__ lpart,
                                                         int n_split, uint16_t* __restrict__ out,
                                                         float* __restrict__ lse) {
@@ -439,8 +489,12 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(const float* __restrict_
     const float wj = __expf(lp[j * DSA_MLA_HEADS] - mx);
     if (wj == 0.f) continue;
     wsum += wj;
-    const float4 x = *reinterpret_cast<const float4*>(
+    // dims 4c .. 4c+3 were written by wave c / 16 of split j
+    const float u = spart[((t * n_split + j) * (kThreads / 64) + threadIdx.x / 16) * DSA_MLA_HEADS + h];
+    const uint2 hx = *reinterpret_cast<const uint2*>(
         opart + ((t * n_split + j) * DSA_MLA_HEADS + h) * DSA_MLA_DV + 4 * threadIdx.x);
+    const float4 x = make_float4(f16_lo(hx.x) * u, f16_hi(hx.x) * u, f16_lo(hx.y) * u,
+                                 f16_hi(hx.y) * u);
     a.x += wj * x.x;
     a.y += wj * x.y;
     a.z += wj * x.z;
@@ -477,11 +531,13 @@ int default_splits(const BatchArgs& b, int k) {
 }
 
 MlaWs mla_ws_layout(const BatchArgs& b, int n_split) {
-  MlaWs w{0, 0, 0};
+  MlaWs w{0, 0, 0, 0};
   if (n_split <= 1) return w;
   size_t off = 0;
-  w.opart_off = off;
-  off = align_up(off + (size_t)b.T * n_split * DSA_MLA_HEADS * DSA_MLA_DV * 4, 256);
+  w.opart_off = off;  // fp16 partials [T][n_split][128][512]
+  off = align_up(off + (size_t)b.T * n_split * DSA_MLA_HEADS * DSA_MLA_DV * 2, 256);
+  w.spart_off = off;  // their scales [T][n_split][8 dim slices][128]
+  off = align_up(off + (size_t)b.T * n_split * (kThreads / 64) * DSA_MLA_HEADS * 4, 256);
   w.lpart_off = off;
   off = align_up(off + (size_t)b.T * n_split * DSA_MLA_HEADS * 4, 256);
   w.total = off;
@@ -505,19 +561,21 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
   const float scale_log2 = sm_scale * kLog2e;
   if (used == 1) {
     hipLaunchKernelGGL((sparse_mla_kernel<false>), dim3(8 * per_xcd), dim3(kThreads), 0, s, b, q,
-                       kv, idx, k, scale_log2, out, lse, (float*)nullptr, (float*)nullptr, 1,
+                       kv, idx, k, scale_log2, out, lse, (uint16_t*)nullptr, (float*)nullptr,
+                       (float*)nullptr, 1,
                        chunk, n_work, per_xcd, idx_mode);
     return hipGetLastError();
   }
   const MlaWs L = mla_ws_layout(b, used);
   char* base = static_cast<char*>(ws);
-  float* opart = reinterpret_cast<float*>(base + L.opart_off);
+  uint16_t* opart = reinterpret_cast<uint16_t*>(base + L.opart_off);
+  float* spart = reinterpret_cast<float*>(base + L.spart_off);
   float* lpart = reinterpret_cast<float*>(base + L.lpart_off);
   hipLaunchKernelGGL((sparse_mla_kernel<true>), dim3(8 * per_xcd), dim3(kThreads), 0, s, b, q, kv,
-                     idx, k, scale_log2, out, lse, opart, lpart, used, chunk, n_work, per_xcd,
+                     idx, k, scale_log2, out, lse, opart, spart, lpart, used, chunk, n_work, per_xcd,
                      idx_mode);
   hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(b.T * DSA_MLA_HEADS)), dim3(128), 0, s,
-                     opart, lpart, used, out, lse);
+                     opart, spart, lpart, used, out, lse);
   return hipGetLastError();
 }
 

@@ -165,7 +165,7 @@ def test_dense_mla_argument_checks(L):
     P = 0x1000
     b = _batch()
     need = L.dsa_workspace_size(B.DSA_OP_DENSE_MLA, ctypes.byref(b), 1, 4)
-    assert need >= 4 * 4 * 128 * 512 * 4  # 4 splits of 4 rows
+    assert need >= 4 * 4 * 128 * 512 * 2  # 4 splits of 4 rows, fp16 partials
     assert L.dsa_dense_mla_decode(ctypes.byref(b), None, P, 0.1, P, None, 4, P, need, None) == \
         B.DSA_ERR_INVALID_ARG
     assert L.dsa_dense_mla_decode(ctypes.byref(b), P, P, 0.1, P, None, 4, P, need - 1, None) == \
@@ -182,7 +182,7 @@ def test_sparse_mla_argument_checks(L):
     assert L.dsa_sparse_mla_decode(ctypes.byref(b), P, P, P, 16, 0.1, P, None, 65, P, 1 << 30,
                                    None) == B.DSA_ERR_INVALID_ARG
     need = L.dsa_workspace_size(B.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 4)
-    assert need >= 4 * 4 * 128 * 512 * 4
+    assert need >= 4 * 4 * 128 * 512 * 2  # fp16 partials of 4 splits x 4 rows
     assert L.dsa_sparse_mla_decode(ctypes.byref(b), P, P, P, 2048, 0.1, P, None, 4, P, need - 1,
                                    None) == B.DSA_ERR_WORKSPACE
     # a single split needs no workspace
