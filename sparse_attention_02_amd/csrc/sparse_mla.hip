@@ -474,36 +474,62 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(const uint16_t* __restri
   const int64_t th = blockIdx.x;  // t * 128 + h
   const int64_t t = th / DSA_MLA_HEADS;
   const int h = (int)(th - t * DSA_MLA_HEADS);
+  const int c = threadIdx.x;  // dims 4c .. 4c+3, written by wave c / 16 of each split
   const float* lp = lpart + t * n_split * DSA_MLA_HEADS + h;
-  float mx = -INFINITY;
-  for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, lp[j * DSA_MLA_HEADS]);
-  uint16_t* o = out + th * DSA_MLA_DV + 4 * threadIdx.x;
+  auto lse_of = [&](int j) { return lp[j * DSA_MLA_HEADS]; };
+  auto scale_of = [&](int j) {
+    return spart[((t * n_split + j) * (kThreads / 64) + c / 16) * DSA_MLA_HEADS + h];
+  };
+  auto part_of = [&](int j) {
+    return *reinterpret_cast<const uint2*>(
+        opart + ((t * n_split + j) * DSA_MLA_HEADS + h) * DSA_MLA_DV + 4 * c);
+  };
+  uint16_t* o = out + th * DSA_MLA_DV + 4 * c;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f, mx = -INFINITY;
+  // split j's share, in ascending j (the order fixes the rounding)
+  auto add = [&](float lj, float u, uint2 hx) {
+    const float wj = __expf(lj - mx);
+    if (wj == 0.f) return;
+    wsum += wj;
+    a.x += wj * (f16_lo(hx.x) * u);
+    a.y += wj * (f16_hi(hx.x) * u);
+    a.z += wj * (f16_lo(hx.y) * u);
+    a.w += wj * (f16_hi(hx.y) * u);
+  };
+  if (n_split <= 4) {
+    // every load issued before any is used
+    float lj[4], u[4];
+    uint2 hx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int jj = min(j, n_split - 1);
+      lj[j] = lse_of(jj);
+      u[j] = scale_of(jj);
+      hx[j] = part_of(jj);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < n_split) mx = fmaxf(mx, lj[j]);
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < n_split) add(lj[j], u[j], hx[j]);
+    }
+  } else {
+    for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, lse_of(j));
+    if (mx != -INFINITY)
+      for (int j = 0; j < n_split; ++j) add(lse_of(j), scale_of(j), part_of(j));
+  }
   if (mx == -INFINITY) {
     *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-    if (lse && threadIdx.x == 0) lse[th] = -INFINITY;
+    if (lse && c == 0) lse[th] = -INFINITY;
     return;
-  }
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  for (int j = 0; j < n_split; ++j) {
-    const float wj = __expf(lp[j * DSA_MLA_HEADS] - mx);
-    if (wj == 0.f) continue;
-    wsum += wj;
-    // dims 4c .. 4c+3 were written by wave c / 16 of split j
-    const float u = spart[((t * n_split + j) * (kThreads / 64) + threadIdx.x / 16) * DSA_MLA_HEADS + h];
-    const uint2 hx = *reinterpret_cast<const uint2*>(
-        opart + ((t * n_split + j) * DSA_MLA_HEADS + h) * DSA_MLA_DV + 4 * threadIdx.x);
-    const float4 x = make_float4(f16_lo(hx.x) * u, f16_hi(hx.x) * u, f16_lo(hx.y) * u,
-                                 f16_hi(hx.y) * u);
-    a.x += wj * x.x;
-    a.y += wj * x.y;
-    a.z += wj * x.z;
-    a.w += wj * x.w;
   }
   const float inv = 1.f / wsum;
   *reinterpret_cast<uint2*>(o) =
       make_uint2(pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv));
-  if (lse && threadIdx.x == 0) lse[th] = mx + logf(wsum);
+  if (lse && c == 0) lse[th] = mx + logf(wsum);
 }
 
 // tokens per split (a multiple of the tile, at most kMaxChunk) and the

@@ -76,6 +76,13 @@ def test_topk_argument_checks(L):
     rc = L.dsa_topk(ctypes.byref(b), P, 300, 16, P, P, need - 1, None)
     assert rc == B.DSA_ERR_WORKSPACE
     assert L.dsa_topk(ctypes.byref(b), P, 300, 16, None, P, need, None) == B.DSA_ERR_INVALID_ARG
+    # rows longer than the final pass's bitmap (393216 positions) are sorted
+    # in LDS, which holds 4096 selections: a larger k is refused up front
+    long = _batch(max_seqlen_k=400000, max_pages=6250)
+    need = L.dsa_workspace_size(B.DSA_OP_TOPK, ctypes.byref(long), 4097, 0)
+    assert L.dsa_topk(ctypes.byref(long), P, 400000, 4097, P, P, need, None) == \
+        B.DSA_ERR_UNSUPPORTED
+    assert "4096" in _err(L)
 
 
 def test_index_score_argument_checks(L):

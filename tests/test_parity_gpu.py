@@ -203,6 +203,30 @@ def test_topk_one_pass_and_multi_pass_agree(L, k, pattern):
     assert np.array_equal(got[0], got[1])
 
 
+@pytest.mark.parametrize("k", [1, 2048, 4096])
+def test_topk_rows_longer_than_the_bitmap(k):
+    """Rows of more than 393216 positions: the final pass gathers the
+    selection into LDS and sorts it (k <= 4096); rounded scores put many
+    keys at the threshold.  Equal to the oracle's selection, ascending."""
+    L = [400000, 450001, 393216]
+    rng = np.random.default_rng(k)
+    meta = _meta(L)
+    T, mx = len(L), max(L)
+    ld = mx + (-mx) % 4
+    s = np.round(rng.normal(size=(T, ld)), 2).astype(np.float32)
+    sel, _, _, Ks = O.topk(s.astype(np.float64), L, k, band=0.0)
+    ws_bytes = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, meta, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(meta, torch.from_numpy(s).cuda(), ld, k, idx, ws, ws_bytes)
+    sync()
+    g = idx.cpu().numpy()
+    for i in range(T):
+        K_ = int(Ks[i])
+        assert g[i, :K_].tolist() == sorted(sel[i, :K_].tolist()), i
+        assert (g[i, K_:] == -1).all()
+
+
 @pytest.mark.parametrize("ci", range(len(SMALL)))
 def test_selection_end_to_end_small(ci):
     b = _small(SMALL[ci], 400 + ci)
