@@ -472,6 +472,40 @@ def short_measure(steps):
     return res
 
 
+def short_prefill_measure(steps, n=4096):
+    """A prefill chunk on an empty cache (n rows, row j sees j + 1 tokens):
+    the sparse step (indexer over the causal n x n block, top-2048, sparse
+    attention) against dense causal attention over every visible token
+    (dsa_dense_mla_decode), the trade-off the pages quote for short
+    prefills.  Different computations beyond 2048 visible tokens: this only
+    times them."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    import synth
+    from synth.device import to_device
+    b = synth.make_batch([n], [n], seed=84, paging="identity", heavy=64, pool_extra_pages=1)
+    d = to_device(b)
+    step = Step(b, d)
+    mk = dsa.dsa_workspace_size(dsa.DSA_OP_DENSE_MLA, d.meta, 1, 0)
+    ws = torch.empty(max(mk, 1), dtype=torch.uint8, device="cuda")
+
+    def dense():
+        dsa.dsa_dense_mla_decode(d.meta, d.q[0], d.kv[0], synth.SM_SCALE, step.out, step.lse, 0,
+                                 ws, mk)
+
+    sparse_ms, dense_ms = [], []
+    for _ in range(3):
+        sparse_ms.append(wall_ms(step, steps))
+        dense_ms.append(wall_ms(dense, steps))
+    res = {"workload": f"prefill-{n}-on-empty-cache", "query_rows": b.T,
+           "ms_sparse_step": min(sparse_ms), "ms_dense_attention": min(dense_ms)}
+    res["sparse_over_dense"] = res["ms_sparse_step"] / res["ms_dense_attention"]
+    del step, d, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def mli_measure(steps):
     """Two-stream MLI step vs the same kernels back to back on one stream."""
     import numpy as np
@@ -636,6 +670,8 @@ def main():
         log(f"mli {result['mli']}")
         result["short_context"] = short_measure(max(5, args.steps // 2))
         log(f"short context {result['short_context']}")
+        result["short_prefill"] = short_prefill_measure(max(3, args.steps // 10))
+        log(f"short prefill {result['short_prefill']}")
         result["cache_append"] = append_measure()
         log(f"cache append {result['cache_append']}")
         result["index_space"] = space

@@ -422,7 +422,8 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (!mli) {
     rc = select(sm);
     if (rc) return rc;
-    return attend(idx_out, dense ? dsa::kMlaDense : dsa::kMlaLogical);
+    // the selection just written is compact (positions first, then -1)
+    return attend(idx_out, dense ? dsa::kMlaDense : dsa::kMlaCompact);
   }
 
   // MLI: attention over the previous indexer layer's selection on the main

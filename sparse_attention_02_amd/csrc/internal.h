@@ -82,7 +82,9 @@ hipError_t launch_cache_append(const BatchArgs& b, const uint16_t* k_new, const 
 
 // What the attention's idx holds: logical positions, physical slots, or
 // nothing (dense: every visible position among the first k, idx unused).
-enum MlaIndex { kMlaLogical = 0, kMlaPaged = 1, kMlaDense = 2 };
+// kMlaCompact: logical positions whose row holds its min(k, v) entries first
+// and -1 after (the top-k's own output), so later entries are not read.
+enum MlaIndex { kMlaLogical = 0, kMlaPaged = 1, kMlaDense = 2, kMlaCompact = 3 };
 hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16_t* kv,
                              const int32_t* idx, int k, float sm_scale, uint16_t* out, float* lse,
                              int n_split, void* ws, hipStream_t s, int idx_mode = kMlaLogical);

@@ -171,7 +171,11 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int bi = row_request(b.cu, b.B, t);
   const int v = row_visible(b, bi, t);
   const int j0 = split * chunk;
-  const int ntok = max(0, min(k, j0 + chunk) - j0);
+  // entries past min(k, v) hold nothing in the dense form and in a compact
+  // selection (the top-k writes its min(k, v) positions first, then -1):
+  // their tiles, and splits made only of them, are skipped outright
+  const int lim = idx_mode == kMlaDense || idx_mode == kMlaCompact ? min(k, v) : k;
+  const int ntok = max(0, min(lim, j0 + chunk) - j0);
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
 
   const int tid = threadIdx.x;
