@@ -5,7 +5,10 @@ absorbed-MLA split-KV decode + LSE merge) over the decode batch of 64
 requests x 2 query rows (1 + MTP) at a 131072-token context, on seeded
 synthetic inputs resident in HBM.  Prints one JSON line.
 
-The step time comes from K back-to-back steps; then K more steps run with
+The step time comes from K back-to-back steps after the W warmup steps
+(extended, untimed, until the GPU has been busy for 0.25 s: its clocks ramp
+over the first ~40 ms of load; `warmup_run` reports how many ran); then K
+more steps run with
 the library recording HIP events around each stage on the stream the stage
 runs on, and the roofline of the dominant kernel (the indexer scan) is its
 algorithmic bytes over the average of those per-launch durations.
@@ -37,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DSA decode query-tokens/s at 128K ctx (indexer+top-2048+sparse MLA), % HBM peak"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+SETTLE_S = 0.25  # least busy time before any timed region
 DECODE_WORKLOAD = 2
 PREFILL_WORKLOAD = 3
 MLI_WORKLOAD = 4
@@ -175,8 +179,18 @@ def timed_steps(step, steps, warmup):
     import torch
 
     import sparse_attention_02_amd as dsa
-    for _ in range(warmup):
+    # the W warmup steps, then more untimed steps until the GPU has been busy
+    # for SETTLE_S: its clocks ramp over the first ~40 ms of load (0.43 ->
+    # 0.37 ms per step on the 128K batch), which a short warmup would leave
+    # inside the timed region
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < warmup or time.perf_counter() - t_w < SETTLE_S:
         step()
+        n_w += 1
+        if n_w % 16 == 0:
+            torch.cuda.synchronize()
+    timed_steps.warmup_run = n_w
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -202,10 +216,17 @@ def percentiles(xs):
     return {"p10": float(p10), "p50": float(p50), "p90": float(p90), "n": len(xs)}
 
 
-def wall_ms(fn, iters, warmup=2):
+def wall_ms(fn, iters, warmup=2, settle_s=0.1):
+    """Wall time per call over `iters` calls, after `warmup` calls and at
+    least `settle_s` of untimed calls (clock ramp after idle time)."""
     import torch
-    for _ in range(warmup):
+    t_w = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t_w < settle_s:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(iters):
@@ -578,8 +599,8 @@ def layers_measure(b, d, steps, n_layers=8):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128,
                     help="query rows the CPU oracle baseline covers (all 128 of the workload: about 10 s)")
@@ -643,6 +664,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": timed_steps.warmup_run,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
