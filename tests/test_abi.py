@@ -236,7 +236,9 @@ def test_workspace_sizes_grow_with_the_batch(L):
         assert L.dsa_workspace_size(op, ctypes.byref(big), 64, 0) > \
             L.dsa_workspace_size(op, ctypes.byref(small), 64, 0)
     assert L.dsa_workspace_size(99, ctypes.byref(small), 64, 0) == 0
-    # about 256 work-groups, at least 4 tiles of 32 tokens per split
+    # at most 256 work-groups, at least 4 tiles of 32 tokens per split
+    assert L.dsa_default_splits(ctypes.byref(_batch(T=96, max_seqlen_k=300)), 2048) == 2
+    assert L.dsa_default_splits(ctypes.byref(_batch(T=300, max_seqlen_k=300)), 2048) == 1
     assert L.dsa_default_splits(ctypes.byref(small), 2048) == 16
     assert L.dsa_default_splits(ctypes.byref(_batch(T=128, max_seqlen_k=300)), 2048) == 2
     assert L.dsa_default_splits(ctypes.byref(_batch(T=32, max_seqlen_k=300)), 2048) == 8
