@@ -271,6 +271,17 @@ def cpu_baseline(batch, rows, threads):
     return time.perf_counter() - t0
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def prefill_measure(steps):
     """Prefill-chunk form: the indexer as a dense causal FP8 contraction."""
     import torch
@@ -711,7 +722,13 @@ def main():
             "kind": "oracle",
             "sample": f"rows 0..{len(rows) - 1} ({len(rows) // 2} requests x 2 rows) of the "
                       f"same workload: float64 index scores over 131072 keys, top-2048, "
-                      f"attention; {secs:.1f} s wall"}
+                      f"attention; {secs:.1f} s wall",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+        if args.extras:
+            # the single-request workload (1 row onto 8192 tokens) on one core
+            import synth
+            b0 = synth.make_workload(0)
+            result["cpu_baseline"]["decode-b1-q1-ctx8192_one_core_s"] = cpu_baseline(b0, [0], 1)
     print(json.dumps(result), flush=True)
 
 
