@@ -390,6 +390,26 @@ def test_workload_decode_step(wi):
         assert hv <= set(g[j].tolist()) or len(hv) > K
 
 
+def test_prefill_chunk_longer_than_the_one_pass_topk():
+    """1024 new rows on a 68976-token prefix (70000 cached): the row-group
+    scan in 128-page ranges with its histogram epilogue, then the
+    multi-kernel top-k (rows of more than 65536 positions).  Scores,
+    selection and attention on sampled rows against the oracle."""
+    b = synth.make_batch([1024], [70000], seed=1600, paging="shuffled", heavy=64,
+                         pool_extra_pages=3)
+    d = to_device(b)
+    idx, out, lse = decode_step(d)
+    scores, ld = index_scores(d)
+    sync()
+    rows = sorted({0, 1023} | set(_sample_rows(b.T, 4, 16)))
+    meta, vis, sc, sel, flags, Ks = oracle_rows(b, rows)
+    check_scores(scores[rows].cpu().numpy().astype(np.float64), sc, vis)
+    g = idx[rows].cpu().numpy()
+    check_selection(g, sel, flags, Ks)
+    ref, ref_lse = O.sparse_mla(meta, b.q[0], b.kv[0], g, rows, synth.SM_SCALE)
+    check_attention(bf16_to_f64(out[rows]), ref, lse[rows].cpu().numpy(), ref_lse)
+
+
 @pytest.mark.parametrize("wi", [1, 2])
 def test_workload_index_scores(wi):
     b, d = _workload(wi)
