@@ -249,7 +249,10 @@ enum {
 
 typedef struct {
   int32_t mode;               /* dsa_step_mode */
-  int32_t n_split;            /* as dsa_sparse_mla_decode (0 = choose) */
+  int32_t n_split;            /* as dsa_sparse_mla_decode (0 = choose; in
+                               * MLI mode the choice keeps the attention to
+                               * half the work-groups of the other modes, so
+                               * the concurrent scan keeps CUs) */
   const int32_t* attend_idx;  /* MLI: int32 [T, k] selection the attention reads */
   /* Optional (NULL = none): 2 * DSA_NUM_STAGES caller-created hipEvent_t.
    * Event 2i is recorded just before stage i and event 2i+1 just after it,
@@ -319,7 +322,8 @@ typedef enum {
  * library's choice, as in the calls).  0 for an invalid request. */
 size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n_split);
 
-/* KV splits the library chooses for a batch when n_split = 0. */
+/* KV splits the library chooses for a batch when n_split = 0 (the single
+ * ops and FUSED steps; MLI steps choose at most this many). */
 int32_t dsa_default_splits(const dsa_batch_t* batch, int32_t k);
 
 const char* dsa_status_string(int status);

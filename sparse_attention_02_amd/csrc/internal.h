@@ -44,7 +44,11 @@ struct MlaWs {
 };
 MlaWs mla_ws_layout(const BatchArgs& b, int n_split);
 
-int default_splits(const BatchArgs& b, int k);
+// KV splits for n_split = 0: at most `wgs` work-groups of the attention
+// (256 fill the CUs; beside a concurrent scan, fewer leave it room).
+constexpr int kAttnWGs = 256;
+constexpr int kAttnWGsShared = 128;
+int default_splits(const BatchArgs& b, int k, int wgs = kAttnWGs);
 
 // KV splits actually launched for k tokens per row and a requested split count.
 int mla_splits_used(int k, int n_split);

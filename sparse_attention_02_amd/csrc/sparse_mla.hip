@@ -548,16 +548,16 @@ void split_shape(int k, int n_split, int* chunk, int* used) {
 
 }  // namespace
 
-int default_splits(const BatchArgs& b, int k) {
-  // at most 256 work-groups over the batch (one per CU: a work-group holds
-  // 156 KB of LDS, so a 257th waits for a whole second round -- 96 rows in 3
-  // splits took 131 us, in 2 splits 96 us), and at least 4 tiles per split: a
+int default_splits(const BatchArgs& b, int k, int wgs) {
+  // at most `wgs` work-groups over the batch (256 = one per CU: a work-group
+  // holds 156 KB of LDS, so a 257th waits for a whole second round -- 96 rows
+  // in 3 splits took 131 us, in 2 splits 96 us), and at least 4 tiles per split: a
   // split's fixed costs (its slot table, the query load, its partial write
   // and its share of the merge) outweigh a tile's work below that (a single
   // row at k = 2048 runs its attention in 37 us with 16 splits, 60 us with 64)
   const int max_by_k = std::max(1, (k + 4 * kMlaTile - 1) / (4 * kMlaTile));
   if (b.T <= 0) return 1;
-  int ns = 256 / b.T;
+  int ns = wgs / b.T;
   ns = std::min(ns, std::min(max_by_k, kMaxSplits));
   return std::max(ns, 1);
 }

@@ -429,9 +429,13 @@ def test_workload_mli_two_stream():
     aux = torch.cuda.Stream()
     sel1, out_mli, lse_mli = decode_step(d, layer=1, mode=dsa.DSA_MODE_MLI, attend_idx=sel0,
                                          mla_layer=0, stream_aux=aux)
+    # with the fused step's split count, the attention of the MLI step equals
+    # the fused step's (same selection, same layer); by default MLI picks fewer
+    ns = dsa.dsa_default_splits(d.meta, K)
+    _, out_ns, lse_ns = decode_step(d, layer=1, mode=dsa.DSA_MODE_MLI, attend_idx=sel0,
+                                    mla_layer=0, n_split=ns, stream_aux=aux)
     sync()
-    # attention of the MLI step equals the fused step's (same selection, same layer)
-    assert torch.equal(out_mli, out0) and torch.equal(lse_mli, lse0)
+    assert torch.equal(out_ns, out0) and torch.equal(lse_ns, lse0)
     rows = _sample_rows(b.T, 6, 44)
     meta, vis, sc1, s1, f1, K1 = oracle_rows(b, rows, layer=1)
     check_selection(sel1[rows].cpu().numpy(), s1, f1, K1)
