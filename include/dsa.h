@@ -100,7 +100,9 @@ typedef struct {
  *           [0, num_pages) (the pool holds no key for them).
  *           With positive scales this equals I(t,s) on the dequantised values.
  *  ld       >= max_seqlen_k
- * Errors: INVALID_ARG (null pointers with T > 0, ld too small, bad scalars). */
+ * q8 and k8_cache must be 16-byte aligned, scores 4-byte.
+ * Errors: INVALID_ARG (null pointers with T > 0, misalignment, ld too small,
+ * bad scalars). */
 int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_scale,
                     const float* w, const uint8_t* k8_cache, const float* k_scale, float* scores,
                     int64_t ld, void* stream);
@@ -180,7 +182,8 @@ int dsa_topk_transform(const dsa_batch_t* batch, const float* scores, int64_t ld
  *           scaled scores (-inf for a row with no valid entry)
  *  n_split  KV splits per row (0 = choose), 1 .. 64
  *  ws       workspace (>= dsa_workspace_size(DSA_OP_SPARSE_MLA, ...))
- * Errors: INVALID_ARG, WORKSPACE. */
+ * q, kv_cache, out and ws must be 16-byte aligned.
+ * Errors: INVALID_ARG (also for misalignment), WORKSPACE. */
 int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
                           const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
                           float* lse, int32_t n_split, void* ws, size_t ws_bytes, void* stream);
@@ -273,7 +276,9 @@ typedef struct {
  *  ws        >= dsa_workspace_size(DSA_OP_DECODE_STEP, ...) bytes
  *  stream_main, stream_aux  stream_aux is used only in MLI mode (must be
  *            non-NULL and differ from stream_main there)
- * Errors: INVALID_ARG, WORKSPACE, HIP. */
+ * mla->q, mla->kv_cache, out, ws, ix->q8 and ix->k8_cache must be 16-byte
+ * aligned.
+ * Errors: INVALID_ARG (also for misalignment), WORKSPACE, HIP. */
 int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
                     const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
                     int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
@@ -305,7 +310,8 @@ typedef struct {
  *  sel      int32 [ceil(n_layers / retention), T, k] out
  *  ws       >= dsa_workspace_size(DSA_OP_DECODE_STEP, batch, k, n_split)
  *  stream_aux  used when mli = 1 (non-NULL, different from stream_main)
- * Every pointer of every layer is checked before anything is enqueued.
+ * Every pointer of every layer is checked (non-NULL, aligned as
+ * dsa_decode_step asks) before anything is enqueued.
  * Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED, HIP. */
 int dsa_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_layer_t* layers,
                       int32_t k, int32_t retention, int32_t mli, int32_t n_split, int32_t* sel,

@@ -67,6 +67,23 @@ StepWs step_layout(const dsa_batch_t* b, int used_splits) {
   return w;
 }
 
+// The attention reads q and gathers latent rows in 16-byte pieces, and the
+// output and the workspace partials move in 16-byte pieces too.
+bool misaligned16(const void* p) { return ((uintptr_t)p & 15) != 0; }
+int check_mla_align(const void* q, const void* kv_cache, const void* out, const void* ws) {
+  if (misaligned16(q) || misaligned16(kv_cache) || misaligned16(out) || misaligned16(ws))
+    return fail(DSA_ERR_INVALID_ARG, "q, kv_cache, out and ws need 16-byte alignment");
+  return DSA_OK;
+}
+
+// The scan reads queries and keys in 16-byte pieces and writes scores in
+// 4-byte ones (16-byte ones where a row is aligned).
+int check_index_align(const void* q8, const void* k8_cache, const float* scores) {
+  if (misaligned16(q8) || misaligned16(k8_cache) || ((uintptr_t)scores & 3) != 0)
+    return fail(DSA_ERR_INVALID_ARG, "q8 and k8_cache need 16-byte, scores 4-byte alignment");
+  return DSA_OK;
+}
+
 int resolve_splits(const dsa_batch_t* b, int32_t k, int32_t n_split, int* used,
                    int wgs = dsa::kAttnWGs) {
   if (n_split < 0 || n_split > dsa::kMaxSplits)
@@ -150,6 +167,10 @@ int dsa_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_laye
     const dsa_layer_t& L = layers[l];
     if (!L.out || !L.mla.q || (keys && !L.mla.kv_cache))
       return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer in a layer");
+    rc = check_mla_align(L.mla.q, L.mla.kv_cache, L.out, ws);
+    if (rc) return rc;
+    if (l % retention == 0 && (rc = check_index_align(L.ix.q8, L.ix.k8_cache, nullptr)))
+      return rc;
     if (l % retention == 0 &&
         (!L.ix.q8 || !L.ix.q_scale || !L.ix.w || (keys && (!L.ix.k8_cache || !L.ix.k_scale))))
       return fail(DSA_ERR_INVALID_ARG, "NULL indexer pointer in an indexer layer");
@@ -222,6 +243,8 @@ int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_
   if (batch->num_tokens == 0 || batch->max_seqlen_k == 0) return DSA_OK;
   if (!q8 || !q_scale || !w || !k8_cache || !k_scale || !scores)
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  rc = check_index_align(q8, k8_cache, scores);
+  if (rc) return rc;
   hipError_t e = dsa::launch_index_score(dsa::batch_args(*batch), q8, q_scale, w, k8_cache,
                                          k_scale, scores, ld, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "index_score launch");
@@ -290,6 +313,8 @@ int mla_common(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_c
   if (!q || !out || (!idx && idx_mode != dsa::kMlaDense) ||
       (!kv_cache && (batch->max_seqlen_k > 0 || idx_mode == dsa::kMlaPaged)))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  rc = check_mla_align(q, kv_cache, out, ws);
+  if (rc) return rc;
   const dsa::BatchArgs a = dsa::batch_args(*batch);
   const size_t need = dsa::mla_ws_layout(a, used).total;
   if (need > 0 && (ws_bytes < need || !ws))
@@ -358,6 +383,10 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   if (!idx_out || !out || !mla->q || !ix->q8 || !ix->q_scale || !ix->w ||
       (batch->max_seqlen_k > 0 && (!ix->k8_cache || !ix->k_scale || !mla->kv_cache)))
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  rc = check_mla_align(mla->q, mla->kv_cache, out, ws);
+  if (rc) return rc;
+  rc = check_index_align(ix->q8, ix->k8_cache, nullptr);
+  if (rc) return rc;
   if (!dsa::topk_supported(dsa::batch_args(*batch), k))
     return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
   const StepWs L = step_layout(batch, used);

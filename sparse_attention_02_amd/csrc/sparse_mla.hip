@@ -470,41 +470,48 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
 
 // out(t,h) = sum_j e^{lse_j - lse*} O_j / sum_j e^{lse_j - lse*},
 // lse(t,h) = lse* + ln sum_j e^{lse_j - lse*}, lse* = max_j lse_j.
-__global__ __launch_bounds__(128) void mla_merge_kernel(const uint16_t* __restrict__ opart,
-                                                        const float* __restrict__ spart,
-                                                        const float* __restrict__ lpart,
-                                                        int n_split, uint16_t* __restrict__ out,
-                                                        float* __restrict__ lse) {
-  const int64_t th = blockIdx.x;  // t * 128 + h
+// One wave per (row, head), four per work-group; lane l holds dims
+// 8l .. 8l+7 (16-byte loads of the fp16 partials, one 16-byte bf16 store).
+constexpr int kMergeWaves = 4;
+
+__global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(
+    const uint16_t* __restrict__ opart, const float* __restrict__ spart,
+    const float* __restrict__ lpart, int n_split, int64_t n_th, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  const int64_t th = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);  // t * 128 + h
+  if (th >= n_th) return;
   const int64_t t = th / DSA_MLA_HEADS;
   const int h = (int)(th - t * DSA_MLA_HEADS);
-  const int c = threadIdx.x;  // dims 4c .. 4c+3, written by wave c / 16 of each split
+  const int l = threadIdx.x & 63;
   const float* lp = lpart + t * n_split * DSA_MLA_HEADS + h;
   auto lse_of = [&](int j) { return lp[j * DSA_MLA_HEADS]; };
+  // the power-of-two scale of this lane's 64-dim slice (written by wave l / 8)
   auto scale_of = [&](int j) {
-    return spart[((t * n_split + j) * (kThreads / 64) + c / 16) * DSA_MLA_HEADS + h];
+    return spart[((t * n_split + j) * (kThreads / 64) + l / 8) * DSA_MLA_HEADS + h];
   };
   auto part_of = [&](int j) {
-    return *reinterpret_cast<const uint2*>(
-        opart + ((t * n_split + j) * DSA_MLA_HEADS + h) * DSA_MLA_DV + 4 * c);
+    return *reinterpret_cast<const uint4*>(
+        opart + ((t * n_split + j) * DSA_MLA_HEADS + h) * DSA_MLA_DV + 8 * l);
   };
-  uint16_t* o = out + th * DSA_MLA_DV + 4 * c;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint16_t* o = out + th * DSA_MLA_DV + 8 * l;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f, mx = -INFINITY;
   // split j's share, in ascending j (the order fixes the rounding)
-  auto add = [&](float lj, float u, uint2 hx) {
+  auto add = [&](float lj, float u, uint4 hx) {
     const float wj = __expf(lj - mx);
     if (wj == 0.f) return;
     wsum += wj;
-    a.x += wj * (f16_lo(hx.x) * u);
-    a.y += wj * (f16_hi(hx.x) * u);
-    a.z += wj * (f16_lo(hx.y) * u);
-    a.w += wj * (f16_hi(hx.y) * u);
+    const uint32_t wd[4] = {hx.x, hx.y, hx.z, hx.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[2 * q] += wj * (f16_lo(wd[q]) * u);
+      a[2 * q + 1] += wj * (f16_hi(wd[q]) * u);
+    }
   };
   if (n_split <= 4) {
     // every load issued before any is used
     float lj[4], u[4];
-    uint2 hx[4];
+    uint4 hx[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int jj = min(j, n_split - 1);
@@ -526,14 +533,15 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(const uint16_t* __restri
       for (int j = 0; j < n_split; ++j) add(lse_of(j), scale_of(j), part_of(j));
   }
   if (mx == -INFINITY) {
-    *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-    if (lse && c == 0) lse[th] = -INFINITY;
+    *reinterpret_cast<uint4*>(o) = make_uint4(0u, 0u, 0u, 0u);
+    if (lse && l == 0) lse[th] = -INFINITY;
     return;
   }
   const float inv = 1.f / wsum;
-  *reinterpret_cast<uint2*>(o) =
-      make_uint2(pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv));
-  if (lse && c == 0) lse[th] = mx + logf(wsum);
+  *reinterpret_cast<uint4*>(o) =
+      make_uint4(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv),
+                 pack_bf16x2(a[4] * inv, a[5] * inv), pack_bf16x2(a[6] * inv, a[7] * inv));
+  if (lse && l == 0) lse[th] = mx + logf(wsum);
 }
 
 // tokens per split (a multiple of the tile, at most kMaxChunk) and the
@@ -606,8 +614,9 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
   hipLaunchKernelGGL((sparse_mla_kernel<true>), dim3(8 * per_xcd), dim3(kThreads), 0, s, b, q, kv,
                      idx, k, scale_log2, out, lse, opart, spart, lpart, used, chunk, n_work, per_xcd,
                      idx_mode);
-  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(b.T * DSA_MLA_HEADS)), dim3(128), 0, s,
-                     opart, spart, lpart, used, out, lse);
+  const int64_t n_th = (int64_t)b.T * DSA_MLA_HEADS;
+  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)((n_th + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(64 * kMergeWaves), 0, s, opart, spart, lpart, used, n_th, out, lse);
   return hipGetLastError();
 }
 

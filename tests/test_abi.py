@@ -265,3 +265,31 @@ def test_stage_events_argument_checked():
     with pytest.raises(ValueError):
         B.dsa_decode_step(None, {}, {}, 16, 0, 0, None, None, None, None, None, 0,
                           stage_events=[1, 2, 3])
+
+
+def test_misaligned_pointers_are_refused(L):
+    """The kernels move queries, keys, latent rows, outputs and partials in
+    16-byte pieces: a pointer off that grid is an argument error, caught
+    before anything is launched (fake addresses; nothing is dereferenced)."""
+    P, M = 0x1000, 0x1008
+    b = _batch()
+    need = L.dsa_workspace_size(B.DSA_OP_SPARSE_MLA, ctypes.byref(b), 16, 2)
+    for q, kv, out, ws in [(M, P, P, P), (P, M, P, P), (P, P, M, P), (P, P, P, M)]:
+        assert L.dsa_sparse_mla_decode(ctypes.byref(b), q, kv, P, 16, 0.1, out, None, 2, ws,
+                                       need, None) == B.DSA_ERR_INVALID_ARG
+        assert "16-byte" in _err(L)
+        assert L.dsa_dense_mla_decode(ctypes.byref(b), q, kv, 0.1, out, None, 2, ws, 1 << 30,
+                                      None) == B.DSA_ERR_INVALID_ARG
+    for q8, k8, sc in [(M, P, P), (P, M, P), (P, P, P + 2)]:
+        assert L.dsa_index_score(ctypes.byref(b), q8, P, P, k8, P, sc, 300, None) == \
+            B.DSA_ERR_INVALID_ARG
+        assert "alignment" in _err(L)
+    opts = B.dsa_step_opts_t(B.DSA_MODE_FUSED, 0, None)
+    need = L.dsa_workspace_size(B.DSA_OP_DECODE_STEP, ctypes.byref(b), 64, 0)
+    for q8, q, out, ws in [(M, P, P, P), (P, M, P, P), (P, P, M, P), (P, P, P, M)]:
+        ix = B.dsa_indexer_inputs_t(q8, P, P, P, P)
+        ml = B.dsa_mla_inputs_t(q, P, 0.07)
+        assert L.dsa_decode_step(ctypes.byref(b), ctypes.byref(ix), ctypes.byref(ml), 64,
+                                 ctypes.byref(opts), P, out, None, ws, need, None, None) == \
+            B.DSA_ERR_INVALID_ARG
+        assert "alignment" in _err(L)
