@@ -140,8 +140,9 @@ int dsa_cache_append(const dsa_batch_t* batch, const uint16_t* k_new, const uint
  *          (ties at the k-th score go to the lower position), stored in
  *          idx[t, 0 .. K_t) in ascending order, followed by -1 in
  *          idx[t, K_t .. k); the output is deterministic.
- *  ws      device workspace of >= dsa_workspace_size(DSA_OP_TOPK, ...) bytes
- * Errors: INVALID_ARG, WORKSPACE. */
+ *  ws      device workspace of >= dsa_workspace_size(DSA_OP_TOPK, ...) bytes,
+ *          16-byte aligned
+ * Errors: INVALID_ARG (also for a misaligned ws), WORKSPACE. */
 int dsa_topk(const dsa_batch_t* batch, const float* scores, int64_t ld, int32_t k, int32_t* idx,
              void* ws, size_t ws_bytes, void* stream);
 

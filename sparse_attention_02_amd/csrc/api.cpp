@@ -288,6 +288,7 @@ int topk_common(const dsa_batch_t* batch, const float* scores, int64_t ld, int32
     return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
   const size_t need = dsa::topk_ws_layout(dsa::batch_args(*batch)).total;
   if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "top-k workspace too small");
+  if (misaligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws needs 16-byte alignment");
   hipError_t e = dsa::launch_topk(dsa::batch_args(*batch), scores, ld, k, idx, ws,
                                   (hipStream_t)stream, space, kv_offsets);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");

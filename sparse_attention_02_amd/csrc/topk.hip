@@ -140,11 +140,16 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* ws
   return before + inc - x;
 }
 
+// VEC: rows 16-byte aligned with ld % 4 == 0, so element 4q + e of a thread
+// is position s0 + 4 tid + 1024 q + e, read in 16-byte loads; else element
+// j is position s0 + tid + 256 j, read one by one.  Which segment position a
+// thread holds changes only the order of the appends, not the selection.
+template <bool VEC>
 __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
     BatchArgs b, const float* __restrict__ scores, int64_t ld, int k,
     const uint32_t* __restrict__ hist1, int32_t* __restrict__ ctrl, int32_t* __restrict__ idx,
     uint2* __restrict__ cand, int64_t cand_stride, uint32_t* __restrict__ hist2) {
-  __shared__ uint32_t h1[kTopkBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kTopkBins];
   __shared__ uint32_t h2[kTopkBins];
   __shared__ uint32_t scan[kCollectThreads];
   __shared__ uint32_t wsum[16];
@@ -158,25 +163,44 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   const float* row = scores + (int64_t)t * ld;
   const bool all = v <= k;  // every visible position is selected
 
-  // the row's first-digit histogram, then the segment's scores: element j
-  // of this thread is position s0 + tid + 256 j (coalesced loads, all
-  // issued before any is used: positions past the row re-read its last
-  // score and are masked below).  The threshold search below runs while
-  // the score loads are in flight.
+  // the row's first-digit histogram (8 bins per thread, two 16-byte loads),
+  // then the segment's scores (coalesced loads, all issued before any is
+  // used: positions past the row re-read its last score or group and are
+  // masked below).  The threshold search below runs while the score loads
+  // are in flight.
   constexpr int kHistPer = kTopkBins / kCollectThreads;
-  uint32_t hv[kHistPer];
-#pragma unroll
-  for (int i = 0; i < kHistPer; ++i)
-    hv[i] = all ? 0u : hist1[(int64_t)t * kTopkBins + threadIdx.x + i * kCollectThreads];
-  uint32_t key[kPerThread];
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    key[j] = float_key(row[min(s0 + (int)threadIdx.x + j * kCollectThreads, v - 1)]);
-#pragma unroll
-  for (int i = 0; i < kHistPer; ++i) {
-    h1[threadIdx.x + i * kCollectThreads] = hv[i];
-    h2[threadIdx.x + i * kCollectThreads] = 0u;
+  static_assert(kHistPer == 8, "two 16-byte histogram loads per thread");
+  uint4 hv[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  if (!all) {
+    const uint4* hp = reinterpret_cast<const uint4*>(hist1 + (int64_t)t * kTopkBins);
+    hv[0] = hp[threadIdx.x];
+    hv[1] = hp[threadIdx.x + kCollectThreads];
   }
+  // position of element j of this thread
+  auto pos_of = [&](int j) {
+    return VEC ? s0 + 4 * (int)threadIdx.x + kCollectThreads * 4 * (j >> 2) + (j & 3)
+               : s0 + (int)threadIdx.x + j * kCollectThreads;
+  };
+  uint32_t key[kPerThread];
+  if (VEC) {
+    const int last = (v - 1) & ~3;  // first position of the row's last 16-byte group
+#pragma unroll
+    for (int q = 0; q < kPerThread / 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          row + min(s0 + 4 * (int)threadIdx.x + kCollectThreads * 4 * q, last));
+      key[4 * q] = float_key(x.x);
+      key[4 * q + 1] = float_key(x.y);
+      key[4 * q + 2] = float_key(x.z);
+      key[4 * q + 3] = float_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) key[j] = float_key(row[min(pos_of(j), v - 1)]);
+  }
+  reinterpret_cast<uint4*>(h1)[threadIdx.x] = hv[0];
+  reinterpret_cast<uint4*>(h1)[threadIdx.x + kCollectThreads] = hv[1];
+#pragma unroll
+  for (int i = 0; i < kHistPer; ++i) h2[threadIdx.x + i * kCollectThreads] = 0u;
   __syncthreads();
   // b1: the first-digit bin holding the K-th largest key (-1: all selected);
   // every segment of the row finds the same bin, the first records it
@@ -193,7 +217,7 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   uint32_t am = 0, em = 0;  // bit j: element j is above / a candidate
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    const int s = s0 + threadIdx.x + j * kCollectThreads;
+    const int s = pos_of(j);
     const int d = (int)(key[j] >> 21);
     if (s < v) {
       if (b1 < 0 || d > b1) am |= 1u << j;
@@ -221,7 +245,7 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   int na = 0, ne = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    const int s = s0 + threadIdx.x + j * kCollectThreads;
+    const int s = pos_of(j);
     if (am & (1u << j)) {
       if (ra + na < (uint32_t)k) out[ra + na] = s;
       ++na;
@@ -705,8 +729,12 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
   uint2* cand = reinterpret_cast<uint2*>(base + L.cand_off);
   const int segs = std::max(1, (b.max_seqlen_k + kTopkSeg - 1) / kTopkSeg);
   dim3 g2(b.T, segs);
-  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k, hist1,
-                     ctrl, idx, cand, (int64_t)b.max_seqlen_k, hist2);
+  if ((reinterpret_cast<uintptr_t>(scores) & 15) == 0 && ld % 4 == 0)
+    hipLaunchKernelGGL(topk_collect_kernel<true>, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k,
+                       hist1, ctrl, idx, cand, (int64_t)b.max_seqlen_k, hist2);
+  else
+    hipLaunchKernelGGL(topk_collect_kernel<false>, g2, dim3(kCollectThreads), 0, s, b, scores, ld,
+                       k, hist1, ctrl, idx, cand, (int64_t)b.max_seqlen_k, hist2);
   hipLaunchKernelGGL(topk_final_kernel, dim3(b.T), dim3(kFinalThreads), 0, s, b, k, ctrl, hist2,
                      idx, cand, (int64_t)b.max_seqlen_k, space, kv_off);
   return hipGetLastError();

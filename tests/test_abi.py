@@ -293,3 +293,7 @@ def test_misaligned_pointers_are_refused(L):
                                  ctypes.byref(opts), P, out, None, ws, need, None, None) == \
             B.DSA_ERR_INVALID_ARG
         assert "alignment" in _err(L)
+    b = _batch()
+    need = L.dsa_workspace_size(B.DSA_OP_TOPK, ctypes.byref(b), 16, 0)
+    assert L.dsa_topk(ctypes.byref(b), P, 300, 16, P, M, need, None) == B.DSA_ERR_INVALID_ARG
+    assert "16-byte" in _err(L)
