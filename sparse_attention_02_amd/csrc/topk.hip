@@ -39,10 +39,11 @@ constexpr int kCtrlAbove = 1;  // positions written as "above"
 constexpr int kCtrlCand = 2;   // candidates appended
 constexpr int kCtrlWords = 4;
 
-__global__ void zero_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+// p 16-byte aligned, n16 16-byte words
+__global__ void zero_kernel(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
        i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ int row_len(const BatchArgs& b, int t) {
@@ -711,9 +712,10 @@ hipError_t launch_topk_zero(const BatchArgs& b, void* ws, hipStream_t s) {
   const TopkWs L = topk_ws_layout(b);
   // histograms and control words start at zero (a fill kernel, not a
   // memset, so the sequence can be captured in a graph)
-  const int64_t nz = (int64_t)(L.cand_off / 4);
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)),
-                     dim3(256), 0, s, static_cast<uint32_t*>(ws), nz);
+  // (cand_off is a multiple of 256 bytes and ws 16-byte aligned)
+  const int64_t nz = (int64_t)(L.cand_off / 16);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 1024)),
+                     dim3(256), 0, s, static_cast<uint4*>(ws), nz);
   return hipGetLastError();
 }
 
