@@ -7,7 +7,7 @@
 //   1. hist1   per-row histogram of the top 11 key bits (LDS histograms added
 //              into global memory).  The fused decode step builds it inside
 //              the indexer scan instead (no extra pass over the scores).
-//   2. collect (row x 8192-score segment): each work-group finds the bin b1
+//   2. collect (row x 4096-score segment): each work-group finds the bin b1
 //              holding the K-th largest key from hist1 (while its score loads
 //              are in flight); keys in bins above b1 are selected outright,
 //              keys in b1 become candidates; one atomic per work-group
@@ -20,6 +20,8 @@
 //              the K positions are written in ascending order (LDS bitmap,
 //              or a bitonic sort for rows longer than the bitmap).
 // The output is deterministic: the selected set in ascending order.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace dsa {
@@ -27,7 +29,14 @@ namespace {
 
 constexpr int kHistThreads = 256;
 constexpr int kCollectThreads = 256;
-constexpr int kPerThread = kTopkSeg / kCollectThreads;  // 32 scores per thread
+#ifndef DSA_COLLECT_SEG
+#define DSA_COLLECT_SEG 4096
+#endif
+constexpr int kCollectSeg = DSA_COLLECT_SEG;                // scores per collect work-group
+constexpr int kPerThread = kCollectSeg / kCollectThreads;   // scores per thread
+static_assert(kPerThread <= 64 && kCollectSeg < 65536, "masks of 64 bits, 16-bit counts");
+// bit masks over a thread's scores
+using SegMask = std::conditional_t<(kPerThread > 32), uint64_t, uint32_t>;
 constexpr int kFinalThreads = 1024;
 constexpr int kBitmapWords = 12288;  // 48 KB: rows up to 393216 positions
 constexpr int kSortCap = 4096;       // bitonic fallback (rows longer than the bitmap)
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   __shared__ uint32_t s_above;
   const int t = blockIdx.x;
   const int v = row_len(b, t);
-  const int s0 = blockIdx.y * kTopkSeg;
+  const int s0 = blockIdx.y * kCollectSeg;
   if (s0 >= v) return;
   const float* row = scores + (int64_t)t * ld;
   const bool all = v <= k;  // every visible position is selected
@@ -215,23 +224,23 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
     b1 = s_bin;
   }
   if (blockIdx.y == 0 && threadIdx.x == 0) ctrl[t * kCtrlWords + kCtrlB1] = b1;
-  uint32_t am = 0, em = 0;  // bit j: element j is above / a candidate
+  SegMask am = 0, em = 0;  // bit j: element j is above / a candidate
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int s = pos_of(j);
     const int d = (int)(key[j] >> 21);
     if (s < v) {
-      if (b1 < 0 || d > b1) am |= 1u << j;
-      else if (d == b1) em |= 1u << j;
+      if (b1 < 0 || d > b1) am |= (SegMask)1 << j;
+      else if (d == b1) em |= (SegMask)1 << j;
     }
   }
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j)
-    if (em & (1u << j)) atomicAdd(&h2[(key[j] >> 10) & (kTopkBins - 1)], 1u);
+    if ((em >> j) & 1) atomicAdd(&h2[(key[j] >> 10) & (kTopkBins - 1)], 1u);
 
   // both counts in one scan: at most 8192 per work-group, so 16 bits each
   uint32_t tot;
-  const uint32_t ex = block_exclusive_sum(((uint32_t)__popc(am) << 16) | (uint32_t)__popc(em),
+  const uint32_t ex = block_exclusive_sum(((uint32_t)__popcll(am) << 16) | (uint32_t)__popcll(em),
                                           wsum, &tot);
   const uint32_t ex_a = ex >> 16, ex_e = ex & 0xffffu;
   const uint32_t tot_a = tot >> 16, tot_e = tot & 0xffffu;
@@ -247,11 +256,11 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int s = pos_of(j);
-    if (am & (1u << j)) {
+    if ((am >> j) & 1) {
       if (ra + na < (uint32_t)k) out[ra + na] = s;
       ++na;
     }
-    if (em & (1u << j)) cl[ne++] = make_uint2(key[j], (uint32_t)s);
+    if ((em >> j) & 1) cl[ne++] = make_uint2(key[j], (uint32_t)s);
   }
   if (b1 >= 0) {
     uint32_t* gh = hist2 + (int64_t)t * kTopkBins;
@@ -729,7 +738,7 @@ hipError_t launch_topk_select(const BatchArgs& b, const float* scores, int64_t l
   uint32_t* hist2 = hist1 + (size_t)b.T * kTopkBins;
   int32_t* ctrl = reinterpret_cast<int32_t*>(base + L.ctrl_off);
   uint2* cand = reinterpret_cast<uint2*>(base + L.cand_off);
-  const int segs = std::max(1, (b.max_seqlen_k + kTopkSeg - 1) / kTopkSeg);
+  const int segs = std::max(1, (b.max_seqlen_k + kCollectSeg - 1) / kCollectSeg);
   dim3 g2(b.T, segs);
   if ((reinterpret_cast<uintptr_t>(scores) & 15) == 0 && ld % 4 == 0)
     hipLaunchKernelGGL(topk_collect_kernel<true>, g2, dim3(kCollectThreads), 0, s, b, scores, ld, k,
