@@ -470,9 +470,9 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
 
 // out(t,h) = sum_j e^{lse_j - lse*} O_j / sum_j e^{lse_j - lse*},
 // lse(t,h) = lse* + ln sum_j e^{lse_j - lse*}, lse* = max_j lse_j.
-// One wave per (row, head), four per work-group; lane l holds dims
+// One wave per (row, head), eight per work-group; lane l holds dims
 // 8l .. 8l+7 (16-byte loads of the fp16 partials, one 16-byte bf16 store).
-constexpr int kMergeWaves = 4;
+constexpr int kMergeWaves = 8;
 
 __global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(
     const uint16_t* __restrict__ opart, const float* __restrict__ spart,
