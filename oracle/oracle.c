@@ -90,6 +90,14 @@ int64_t oracle_slot(const oracle_batch* bt, int32_t b, int64_t s) {
   return page * bt->page_size + s % bt->page_size;
 }
 
+/* A page id outside the pool [0, num_pages) names no cached token: the
+ * positions it maps hold no key and no latent row (reading taken here, as
+ * the pages' page tables only ever name allocated pages). */
+int oracle_page_valid(const oracle_batch* bt, int32_t b, int64_t s, int64_t num_pages) {
+  int64_t page = bt->page_table[(int64_t)b * bt->max_pages + s / bt->page_size];
+  return page >= 0 && page < num_pages;
+}
+
 /* ---- work splitting ------------------------------------------------------ */
 
 typedef void (*item_fn)(void* ctx, int64_t item);
@@ -143,6 +151,9 @@ static void run_items(int64_t n, int threads, item_fn fn, void* ctx) {
  * I(t,s) = sum_h w(t,h) * max(0, sum_d q(t,h,d) * k(s,d)) with
  * q = q_scale(t) * e4m3(q8), k = k_scale(s) * e4m3(k8); d and h summed in
  * ascending order.  Written for s < v_t; other entries are left as they are.
+ * A position on a page outside the pool has no key: it scores -infinity, so
+ * it ranks below every real score (and is selected only by a row with fewer
+ * than k keyed positions).
  */
 #define KEY_CHUNK 4096
 
@@ -159,6 +170,7 @@ typedef struct {
   double* out;
   int64_t ld;
   int64_t chunks_per_row;
+  int64_t num_pages;
 } score_ctx;
 
 static void score_item(void* p, int64_t item) {
@@ -178,6 +190,10 @@ static void score_item(void* p, int64_t item) {
   for (int64_t e = 0; e < (int64_t)H * D; ++e)
     q[e] = qs * oracle_e4m3_decode(c->q8[(int64_t)t * H * D + e]);
   for (int64_t s = s0; s < s1; ++s) {
+    if (!oracle_page_valid(c->bt, b, s, c->num_pages)) {
+      c->out[i * c->ld + s] = -INFINITY;
+      continue;
+    }
     int64_t slot = oracle_slot(c->bt, b, s);
     double ks = (double)c->k_scale[slot];
     for (int d = 0; d < D; ++d) k[d] = ks * oracle_e4m3_decode(c->k8[slot * D + d]);
@@ -194,17 +210,17 @@ static void score_item(void* p, int64_t item) {
   free(k);
 }
 
-void oracle_index_score(const oracle_batch* bt, int32_t H, int32_t D, const uint8_t* q8,
-                        const float* q_scale, const float* w, const uint8_t* k8,
-                        const float* k_scale, const int32_t* rows, int32_t n_rows, double* out,
-                        int64_t ld, int threads) {
+void oracle_index_score(const oracle_batch* bt, int64_t num_pages, int32_t H, int32_t D,
+                        const uint8_t* q8, const float* q_scale, const float* w,
+                        const uint8_t* k8, const float* k_scale, const int32_t* rows,
+                        int32_t n_rows, double* out, int64_t ld, int threads) {
   int64_t maxv = 0;
   for (int32_t i = 0; i < n_rows; ++i) {
     int64_t v = oracle_row_visible(bt, rows[i]);
     if (v > maxv) maxv = v;
   }
   score_ctx c = {bt, H, D, q8, q_scale, w, k8, k_scale, rows, n_rows, out, ld,
-                 (maxv + KEY_CHUNK - 1) / KEY_CHUNK};
+                 (maxv + KEY_CHUNK - 1) / KEY_CHUNK, num_pages};
   if (c.chunks_per_row == 0) return;
   run_items((int64_t)n_rows * c.chunks_per_row, threads, score_item, &c);
 }
@@ -285,7 +301,8 @@ void oracle_topk_rows(const double* scores, int64_t ld, const int64_t* v, int32_
  *   p(s) = exp(z(s) - m) / sum_{s'} exp(z(s') - m),  m = max z
  *   o(t,h,d) = sum_s p(s) * kv(s,d)  for d < Dv (Dv = 512)
  *   lse(t,h) = m + ln sum_s exp(z(s) - m)
- * An empty S gives o = 0 and lse = -inf.
+ * An empty S gives o = 0 and lse = -inf.  Positions on a page outside the
+ * pool have no latent row and are left out of S.
  */
 typedef struct {
   const oracle_batch* bt;
@@ -298,6 +315,7 @@ typedef struct {
   const int32_t* rows;
   double* out;
   double* lse;
+  int64_t num_pages;
 } mla_ctx;
 
 static void mla_item(void* p, int64_t item) {
@@ -318,10 +336,11 @@ static void mla_item(void* p, int64_t item) {
   if (c->idx) {
     for (int32_t j = 0; j < c->k; ++j) {
       int32_t s = c->idx[i * c->k + j];
-      if (s >= 0 && s < v) S[n++] = s;
+      if (s >= 0 && s < v && oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
     }
   } else {
-    for (int64_t s = 0; s < v; ++s) S[n++] = s;
+    for (int64_t s = 0; s < v; ++s)
+      if (oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
   }
   if (n == 0) {
     c->lse[i * c->H + h] = -INFINITY;
@@ -356,19 +375,19 @@ static void mla_item(void* p, int64_t item) {
   free(S);
 }
 
-void oracle_sparse_mla(const oracle_batch* bt, int32_t H, int32_t D, int32_t Dv,
-                       const uint16_t* q, const uint16_t* kv, const int32_t* idx, int32_t k,
-                       double sm_scale, const int32_t* rows, int32_t n_rows, double* out,
-                       double* lse, int threads) {
-  mla_ctx c = {bt, H, D, Dv, q, kv, idx, k, sm_scale, rows, out, lse};
+void oracle_sparse_mla(const oracle_batch* bt, int64_t num_pages, int32_t H, int32_t D,
+                       int32_t Dv, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                       int32_t k, double sm_scale, const int32_t* rows, int32_t n_rows,
+                       double* out, double* lse, int threads) {
+  mla_ctx c = {bt, H, D, Dv, q, kv, idx, k, sm_scale, rows, out, lse, num_pages};
   run_items((int64_t)n_rows * H, threads, mla_item, &c);
 }
 
 /* Dense MLA: the same attention over every visible position. */
-void oracle_dense_mla(const oracle_batch* bt, int32_t H, int32_t D, int32_t Dv, const uint16_t* q,
-                      const uint16_t* kv, double sm_scale, const int32_t* rows, int32_t n_rows,
-                      double* out, double* lse, int threads) {
-  mla_ctx c = {bt, H, D, Dv, q, kv, NULL, 0, sm_scale, rows, out, lse};
+void oracle_dense_mla(const oracle_batch* bt, int64_t num_pages, int32_t H, int32_t D, int32_t Dv,
+                      const uint16_t* q, const uint16_t* kv, double sm_scale, const int32_t* rows,
+                      int32_t n_rows, double* out, double* lse, int threads) {
+  mla_ctx c = {bt, H, D, Dv, q, kv, NULL, 0, sm_scale, rows, out, lse, num_pages};
   run_items((int64_t)n_rows * H, threads, mla_item, &c);
 }
 

@@ -55,12 +55,13 @@ def lib():
         L.oracle_bf16_decode.restype = dbl
         L.oracle_row_visible.argtypes = [bp, i32]
         L.oracle_row_visible.restype = i64
-        L.oracle_index_score.argtypes = [bp, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, ci]
+        L.oracle_index_score.argtypes = [bp, i64, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, ci]
         L.oracle_topk.argtypes = [vp, i64, i32, dbl, vp, vp, vp]
         L.oracle_topk.restype = i32
         L.oracle_topk_rows.argtypes = [vp, i64, vp, i32, i32, dbl, vp, vp, i64, vp, vp, ci]
-        L.oracle_sparse_mla.argtypes = [bp, i32, i32, i32, vp, vp, vp, i32, dbl, vp, i32, vp, vp, ci]
-        L.oracle_dense_mla.argtypes = [bp, i32, i32, i32, vp, vp, dbl, vp, i32, vp, vp, ci]
+        L.oracle_sparse_mla.argtypes = [bp, i64, i32, i32, i32, vp, vp, vp, i32, dbl, vp, i32, vp, vp,
+                                        ci]
+        L.oracle_dense_mla.argtypes = [bp, i64, i32, i32, i32, vp, vp, dbl, vp, i32, vp, vp, ci]
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_cache_append.argtypes = [bp, i32, i32, i32, vp, vp, vp, vp, vp]
@@ -125,7 +126,8 @@ def cache_append(meta: Meta, num_pages: int, k_new, kv_new, k8, k_scale, kv):
 
 
 def index_score(meta: Meta, q8, q_scale, w, k8, k_scale, rows, ld=None, threads=0):
-    """float64 scores [len(rows), ld]; entries s >= v_t are NaN."""
+    """float64 scores [len(rows), ld]; entries s >= v_t are NaN.  The pool
+    holds k8.shape[0] pages; positions on a page id outside it score -inf."""
     q8 = np.ascontiguousarray(q8, np.uint8)
     H, D = q8.shape[1], q8.shape[2]
     rows = np.ascontiguousarray(rows, np.int32)
@@ -136,8 +138,8 @@ def index_score(meta: Meta, q8, q_scale, w, k8, k_scale, rows, ld=None, threads=
     ww = np.ascontiguousarray(w, np.float32)
     kk = np.ascontiguousarray(k8, np.uint8)
     ks = np.ascontiguousarray(k_scale, np.float32)
-    lib().oracle_index_score(meta.ref(), H, D, _p(q8), _p(qs), _p(ww), _p(kk), _p(ks), _p(rows),
-                             len(rows), _p(out), ld, threads)
+    lib().oracle_index_score(meta.ref(), kk.shape[0], H, D, _p(q8), _p(qs), _p(ww), _p(kk), _p(ks),
+                             _p(rows), len(rows), _p(out), ld, threads)
     return out
 
 
@@ -159,7 +161,8 @@ def topk(scores_rows, visible, k, band=TIE_BAND, threads=0):
 
 
 def sparse_mla(meta: Meta, q, kv, idx, rows, sm_scale, dv=512, threads=0):
-    """float64 (out [n, H, dv], lse [n, H]) over the positions idx[i] (-1 = none)."""
+    """float64 (out [n, H, dv], lse [n, H]) over the positions idx[i] (-1 = none);
+    positions on a page id outside the kv.shape[0] pages of the pool are left out."""
     q = np.ascontiguousarray(q, np.uint16)
     kv = np.ascontiguousarray(kv, np.uint16)
     H, D = q.shape[1], q.shape[2]
@@ -167,8 +170,9 @@ def sparse_mla(meta: Meta, q, kv, idx, rows, sm_scale, dv=512, threads=0):
     rows = np.ascontiguousarray(rows, np.int32)
     out = np.empty((len(rows), H, dv), np.float64)
     lse = np.empty((len(rows), H), np.float64)
-    lib().oracle_sparse_mla(meta.ref(), H, D, dv, _p(q), _p(kv), _p(idx), idx.shape[1],
-                            float(sm_scale), _p(rows), len(rows), _p(out), _p(lse), threads)
+    lib().oracle_sparse_mla(meta.ref(), kv.shape[0], H, D, dv, _p(q), _p(kv), _p(idx),
+                            idx.shape[1], float(sm_scale), _p(rows), len(rows), _p(out), _p(lse),
+                            threads)
     return out, lse
 
 
@@ -179,8 +183,8 @@ def dense_mla(meta: Meta, q, kv, rows, sm_scale, dv=512, threads=0):
     rows = np.ascontiguousarray(rows, np.int32)
     out = np.empty((len(rows), H, dv), np.float64)
     lse = np.empty((len(rows), H), np.float64)
-    lib().oracle_dense_mla(meta.ref(), H, D, dv, _p(q), _p(kv), float(sm_scale), _p(rows),
-                           len(rows), _p(out), _p(lse), threads)
+    lib().oracle_dense_mla(meta.ref(), kv.shape[0], H, D, dv, _p(q), _p(kv), float(sm_scale),
+                           _p(rows), len(rows), _p(out), _p(lse), threads)
     return out, lse
 
 
@@ -190,8 +194,10 @@ def selection_check(gpu_idx, sel, flags, K):
 
     Returns a list of problems (empty when the row passes)."""
     g = np.asarray(gpu_idx)
-    g = g[g >= 0]
     probs = []
+    if np.any(g < -1):
+        probs.append("entries below -1 (neither a position nor padding)")
+    g = g[g >= 0]
     if len(g) != int(K):
         probs.append(f"count {len(g)} != {int(K)}")
     if len(np.unique(g)) != len(g):

@@ -395,6 +395,64 @@ def test_topk_tie_band_flags():
     assert flags[0].tolist() == [0, 1, 1, 1, 1, 0]
 
 
+def _contract_case():
+    """Twelve visible positions (two rows' worth of columns, ld 14), k = 5.
+    The top five are 0, 7, 2, 11, 5; the k-th score is 5.0004, so the 1e-3
+    band holds positions 5 (5.0004), 4 (5.0) and 10 (4.9998)."""
+    vals = np.array([9.0, 1.0, 7.0, 3.0, 5.0, 5.0004, 2.0, 8.0, 4.0, 0.5, 4.9998, 6.0, 10.0, 11.0])
+    sel, flags, kth, K = O.topk(vals[None, :], [12], 5)
+    assert sel[0].tolist() == [0, 7, 2, 11, 5] and K[0] == 5 and kth[0] == 5.0004
+    assert np.nonzero(flags[0])[0].tolist() == [4, 5, 10]
+    return sel[0], flags[0], int(K[0])
+
+
+@pytest.mark.parametrize("gpu, ok", [
+    ([11, 5, 2, 7, 0], True),              # the oracle's set, another order
+    ([0, 7, 2, 11, 5, -1, -1], True),      # with -1 padding
+    ([0, 7, 2, 11, 4], True),              # swap inside the tie band
+    ([10, 7, 2, 11, 0], True),             # the other band member
+    ([0, 7, 2, 4, 5], False),              # 11 (outside the band) missing
+    ([0, 7, 2, 11, 8], False),             # 8 (outside the band) extra
+    ([0, 7, 2, 11, 11], False),            # duplicate
+    ([0, 7, 2, 11, 13], False),            # position past the row's 12 visible
+    ([0, 7, 2, 11], False),                # short count
+    ([0, 7, 2, 11, 5, 4], False),          # one too many
+    ([0, 7, 2, 11, -5], False),            # an entry that is neither a position nor -1
+])
+def test_selection_check_rejects_known_bad_selections(gpu, ok):
+    """The index contract of the DSA bullet of "MTP and sparse attention: NSA
+    and DSA" (each row keeps its top 2048) with the 1e-3 tie band: the checker
+    accepts the oracle's set in any order and swaps inside the band, and
+    reports every planted defect."""
+    sel, flags, K = _contract_case()
+    probs = O.selection_check(np.array(gpu, np.int32), sel, flags, K)
+    assert (probs == []) == ok, probs
+
+
+def test_index_score_pages_outside_pool_score_minus_inf():
+    """A page id outside the pool (negative, or >= num_pages) names no key:
+    every visible position on it scores -inf; all other scores are unchanged."""
+    b = synth.make_batch([2], [300], seed=21, paging="shuffled", with_mla=False)
+    meta = O.Meta.of(b)
+    good = O.index_score(meta, b.q8, b.q_scale, b.w, b.k8[0], b.k_scale[0], [0, 1])
+    pt = b.page_table.copy()
+    pt[0, 1] = -1
+    pt[0, 3] = b.num_pages
+    bad = O.index_score(O.Meta(b.cu_seqlens_q, b.seqlens_k, pt), b.q8, b.q_scale, b.w, b.k8[0],
+                        b.k_scale[0], [0, 1])
+    invalid = np.zeros(bad.shape[1], bool)
+    invalid[64:128] = invalid[192:256] = True
+    for i, v in enumerate([299, 300]):
+        assert np.all(np.isneginf(bad[i, :v][invalid[:v]]))
+        assert np.array_equal(bad[i, :v][~invalid[:v]], good[i, :v][~invalid[:v]])
+        assert np.all(np.isfinite(good[i, :v]))
+    # the top-k ranks them last: a row with fewer keyed positions than k
+    # takes every keyed one, then the -inf positions by position
+    sel, flags, kth, K = O.topk(np.nan_to_num(bad, nan=-np.inf), [299, 300], 200)
+    keyed = set(np.nonzero(~invalid[:300])[0].tolist())
+    assert keyed - {299} <= set(sel[0, :K[0]].tolist())
+
+
 # ---------------------------------------------------------------- attention
 
 def _mla_case(rng, L, n_q=1, scale=1.0, pages=None):
@@ -502,6 +560,26 @@ def test_sparse_mla_ignores_positions_outside_visible_range():
     o, l = O.sparse_mla(meta, b.q[0], b.kv[0], sel, [0, 1], synth.SM_SCALE)
     o0, l0 = O.sparse_mla(meta, b.q[0], b.kv[0], sel[:, :2], [0, 1], synth.SM_SCALE)
     assert np.array_equal(o[0], o0[0]) and not np.array_equal(o[1], o0[1])
+
+
+def test_sparse_mla_leaves_out_pages_outside_pool():
+    """Selected positions on a page id outside the pool have no latent row:
+    the attention over them equals the attention over the rest, bit for bit."""
+    rng = np.random.default_rng(14)
+    b = _mla_case(rng, 330, scale=1.0)
+    pt = b.page_table.copy()
+    pt[0, 2] = -3
+    pt[0, 4] = b.num_pages + 9
+    meta_bad = O.Meta(b.cu_seqlens_q, b.seqlens_k, pt)
+    sel = np.array([[5, 130, 140, 200, 260, 300, 329]], np.int32)
+    keep = np.array([[5, 200, 329, -1, -1, -1, -1]], np.int32)
+    o1, l1 = O.sparse_mla(meta_bad, b.q[0], b.kv[0], sel, [0], synth.SM_SCALE)
+    o2, l2 = O.sparse_mla(O.Meta.of(b), b.q[0], b.kv[0], keep, [0], synth.SM_SCALE)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    d1, dl1 = O.dense_mla(meta_bad, b.q[0], b.kv[0], [0], synth.SM_SCALE)
+    live = np.array([s for s in range(330) if s // 64 not in (2, 4)], np.int32)[None, :]
+    d2, dl2 = O.sparse_mla(O.Meta.of(b), b.q[0], b.kv[0], live, [0], synth.SM_SCALE)
+    assert np.array_equal(d1, d2) and np.array_equal(dl1, dl2)
 
 
 # ---------------------------------------------------------------- accounting
