@@ -27,7 +27,10 @@
  *  - Host scalars are validated; device metadata (cu_seqlens_q, seqlens_k,
  *    page_table, idx) is trusted to be consistent with them, and kernels
  *    clamp it so a bad value never reads outside the buffers the host
- *    scalars describe (bad positions are treated as not visible).
+ *    scalars describe.  A page id outside [0, num_pages) names no cached
+ *    token: its positions score -inf in the indexer (below every real
+ *    score, so a row selects them only when it has fewer than k keyed
+ *    positions) and the attention skips them.
  *  - Every function returns a dsa_status; on error nothing is enqueued and
  *    dsa_last_error() returns a message (thread-local).  No exception or
  *    abort crosses the ABI.
@@ -95,9 +98,9 @@ typedef struct {
  *  k_scale  f32 [num_pages, 64]    one positive scale per cached key
  *  scores   f32 [T, ld] out: scores[t, s] = q_scale[t] * k_scale[slot(s)] *
  *           sum_h w[t,h] * max(0, sum_d e4m3(q8[t,h,d]) * e4m3(k8[slot(s),d]))
- *           for s < v_t (row t's visible length); entries s >= v_t are not
- *           written, nor are the positions of a page whose id is outside
- *           [0, num_pages) (the pool holds no key for them).
+ *           for s < v_t (row t's visible length), and -inf for the positions
+ *           of a page whose id is outside [0, num_pages) (the pool holds no
+ *           key for them); entries s >= v_t are not written.
  *           With positive scales this equals I(t,s) on the dequantised values.
  *  ld       >= max_seqlen_k
  * q8 and k8_cache must be 16-byte aligned, scores 4-byte.
@@ -242,6 +245,9 @@ typedef enum {
    * waits for stream_aux before the call's work counts as done. */
   DSA_MODE_MLI = 1
 } dsa_step_mode;
+/* In MLI mode the aux stream's top-k writes idx_out while the main stream's
+ * attention reads attend_idx, so the two ranges [ptr, ptr + T*k) must not
+ * overlap (dsa_decode_step returns DSA_ERR_INVALID_ARG when they do). */
 
 /* Stages of a step, in the order of the optional stage events. */
 enum {

@@ -374,6 +374,13 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   const bool mli = opts->mode == DSA_MODE_MLI;
   if (mli && (!opts->attend_idx || !stream_aux || stream_aux == stream_main))
     return fail(DSA_ERR_INVALID_ARG, "MLI mode needs attend_idx and a second stream");
+  if (mli && idx_out) {
+    // the aux stream writes idx_out while the main stream reads attend_idx
+    const uintptr_t a0 = (uintptr_t)opts->attend_idx, i0 = (uintptr_t)idx_out;
+    const uintptr_t n = (uintptr_t)batch->num_tokens * (uintptr_t)k * sizeof(int32_t);
+    if (n > 0 && a0 < i0 + n && i0 < a0 + n)
+      return fail(DSA_ERR_INVALID_ARG, "attend_idx overlaps idx_out in MLI mode");
+  }
   // in MLI mode the attention shares the GPU with the scan on the other
   // stream: by default it takes half the CUs (the ragged 96-row batch: two
   // streams 0.226 ms with 1 split, 0.243 ms with 2)

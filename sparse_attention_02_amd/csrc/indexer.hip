@@ -40,15 +40,17 @@ constexpr int kChunkLargeMinWGs = 2048;
 #ifndef DSA_SCAN_SHARED_TARGET_WGS
 #define DSA_SCAN_SHARED_TARGET_WGS 2048
 #endif
-#ifndef DSA_SCAN_NPF1
-#define DSA_SCAN_NPF1 2
+// 1 KB key loads in flight per wave of the page form (one or two rows):
+// two pages (16) took 202.6 us on the 128K batch, 20 took 207.1, 24 took 204.8
+#ifndef DSA_SCAN_QN1
+#define DSA_SCAN_QN1 16
 #endif
-#ifndef DSA_SCAN_NPF2
-#define DSA_SCAN_NPF2 2
+#ifndef DSA_SCAN_QN2
+#define DSA_SCAN_QN2 16
 #endif
 constexpr int kScanTargetWGs = DSA_SCAN_TARGET_WGS;
-constexpr int kScanNPF1 = DSA_SCAN_NPF1;
-constexpr int kScanNPF2 = DSA_SCAN_NPF2;
+constexpr int kScanQN1 = DSA_SCAN_QN1;
+constexpr int kScanQN2 = DSA_SCAN_QN2;
 #ifndef DSA_SCAN_STAGE_PAGES
 #define DSA_SCAN_STAGE_PAGES 128
 #endif
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
   }
 
   // page i of the chunk (past the end: the last page again; bad ids read
-  // page 0 and are not stored)
+  // page 0 and score -inf)
   const int32_t* ptab = b.pages + (int64_t)bi * b.max_pages;
   const int lane_key = 16 * wave + j;
   auto page_id = [&](int i) { return ptab[min(p_begin + i, p_end - 1)]; };
@@ -197,8 +199,9 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     for (int r = 1; r < RG; ++r)
       if (g == r) mine = sum[r];
     const int s = (p_begin + i) * DSA_PAGE_SIZE + 16 * wave + j;
-    if (page_ok(page_id(i)) && p_begin + i < p_end && g < nr && s < vis_g) {
-      const float sc = mine * qs_g * kscur;
+    if (p_begin + i < p_end && g < nr && s < vis_g) {
+      // a page whose id is outside the pool holds no keys: -inf
+      const float sc = page_ok(page_id(i)) ? mine * qs_g * kscur : -INFINITY;
       srow[s] = sc;
       if (HIST) atomicAdd(&lh[g * kTopkBins + (float_key(sc) >> 21)], 1u);
     }
@@ -237,9 +240,20 @@ hipError_t launch_rg(dim3 grid, hipStream_t s, const BatchArgs& b, const uint8_t
 // permlane32 / permlane16 swaps, with no LDS.  Keys arrive through buffer
 // loads whose descriptor spans exactly one page: a page past the wave's range
 // or with an id outside the pool gets a zero-size descriptor, so its loads
-// return zeros without touching memory and nothing is stored for it.
+// return zeros without touching memory.
+//
+// Each key load is contiguous: lane l reads bytes 16 l .. 16 l + 15 of a
+// 1 KB run (eight whole keys), so a 16-lane quarter of the wave touches two
+// 128-byte lines.  Loading the MFMA operand layout directly (lane (j, g)
+// reading 16 bytes of key j) touches sixteen lines per quarter and held a
+// load-only copy of the scan at 192 us on the 128K batch against 162 us for
+// contiguous loads.  A wave turns each 2 KB column tile into the operand
+// layout through its own 2 KB of LDS (one write and one read of 16 bytes
+// per lane and half-tile); the buffer is XOR-swizzled so that the writes
+// have no bank conflicts.
 constexpr int kPageWaves = 4;
 constexpr int kPageKeyBytes = DSA_PAGE_SIZE * DSA_IDX_DIM;
+constexpr int kTileBytes = 16 * DSA_IDX_DIM;  // one column tile: 16 keys
 constexpr int kBufNT = 2;  // nontemporal cache policy of a buffer load
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -262,15 +276,22 @@ __device__ __forceinline__ float reduce_scatter4(const float p[4]) {
   return __uint_as_float(d[0]) + __uint_as_float(d[1]);
 }
 
-template <int RG, int NPF, bool HIST, int STAGE>
+template <int RG, int QN, bool HIST, int STAGE>
 __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
     BatchArgs b, const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, float* __restrict__ scores, int64_t ld,
     uint32_t* __restrict__ hist, int chunk_pages) {
-  __shared__ uint32_t lh[HIST ? RG * kTopkBins : 1];
+  // first-digit histogram of each row, two 16-bit counts per word (a
+  // work-group scores at most STAGE * 64 <= 8192 positions of a row, so no
+  // count reaches 2^16)
+  static_assert(STAGE * DSA_PAGE_SIZE < 65536, "16-bit histogram counts");
+  __shared__ uint32_t lh[HIST ? RG * kTopkBins / 2 : 1];
   // the work-group's scores, written out in one burst at the end
   __shared__ float lsc[RG][STAGE * DSA_PAGE_SIZE];
+  // each wave's column tile in transit from the load layout to the operand
+  // layout
+  __shared__ __attribute__((aligned(16))) uint8_t ltr[kPageWaves][kTileBytes];
   const int chunk = blockIdx.x;
   const int bi = blockIdx.y;
   const int c0 = b.cu[bi];
@@ -288,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
   const int j = lane & 15;
   const int g = lane >> 4;
   if (HIST) {
-    for (int i = threadIdx.x; i < RG * kTopkBins; i += kThreads) lh[i] = 0u;
+    for (int i = threadIdx.x; i < RG * kTopkBins / 2; i += kThreads) lh[i] = 0u;
   }
 
   // the wave's pages are p_begin + wave + 4i, i < np (np <= 64: one id per lane)
@@ -316,24 +337,26 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
     vis[r] = r < n ? min(L, max(0, L - n + 1 + r)) : 0;
   }
 
-  // key ring: NPF pages in flight per wave.  Page i + NPF is loaded into
-  // the registers of page i tile by tile, right after that tile's MFMAs have
-  // read them, so no register of the ring is ever copied (a copy would wait
-  // for the load in flight).
-  const int koff = j * DSA_IDX_DIM + 32 * g;  // + 2048 c for column tile c
-  v8i kf[NPF][4];
-  float ksr[NPF];
-  int pgr[NPF];
+  // key ring: QN 1 KB loads in flight per wave.  Load x of a page holds keys
+  // 8x .. 8x+7 (lane l: key 8x + l/8, bytes 16 (l % 8) .. 16 (l % 8) + 15).
+  // Chunk q of the wave's stream (page q / 8, load q % 8) lives in register
+  // set q % QN; as soon as a pair of chunks has been handed to the tile
+  // transposition, its registers take chunks q + QN and q + QN + 1, so no
+  // register of the ring is copied.  The page loop is unrolled over GP pages
+  // (one full turn of the ring), which makes every register index static.
+  static_assert(QN % 2 == 0 && QN >= 8 && QN <= 32, "ring of 8 .. 32 chunks");
+  constexpr int GP = (QN % 8 == 0 ? QN : (QN % 4 == 0 ? 2 * QN : 4 * QN)) / 8;
+  v4i kr[QN];
+  float ksr[GP];
   auto key_rsrc = [&](int pg) {
     const bool ok = page_ok(pg);
     return page_rsrc(k8 + (int64_t)(ok ? pg : 0) * kPageKeyBytes, ok ? kPageKeyBytes : 0);
   };
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t kr, int c) {
-    // column tile c's offset rides in the scalar offset, so all tiles share
-    // one address register
-    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 2048 * c, kBufNT);
-    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16, 2048 * c, kBufNT);
-    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int voff = 16 * lane;
+  auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int x) {
+    // the 1 KB offset rides in the scalar offset, so all loads share one
+    // address register
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 1024 * x, kBufNT);
   };
   auto load_scale = [&](int pg) {
     const bool ok = page_ok(pg);
@@ -341,40 +364,58 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
         k_scale + (int64_t)(ok ? pg : 0) * DSA_PAGE_SIZE, ok ? DSA_PAGE_SIZE * 4 : 0);
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, 4 * lane, 0, kBufNT));
   };
+  // transposition: key kk's 16-byte chunk ch sits at kk * 128 + 16 * (ch ^
+  // 2 ((kk / 2) % 4)).  The swizzle leaves the pairs (2p, 2p + 1) in order
+  // and ignores key bit 3, so the second half-tile's write and the second
+  // operand read are immediate offsets of the first (1024 and 16 bytes).
+  // Writes are free of bank conflicts; the operand reads conflict two-way.
+  uint8_t* tw = ltr[wave];
+  const int w_ofs = (lane >> 3) * DSA_IDX_DIM + (((lane & 7) ^ (2 * ((lane >> 4) & 3))) << 4);
+  const int r_ofs = j * DSA_IDX_DIM + (((2 * g) ^ (2 * ((j >> 1) & 3))) << 4);
+  auto transpose = [&](v4i lo_half, v4i hi_half) {
+    *reinterpret_cast<v4i*>(tw + w_ofs) = lo_half;
+    *reinterpret_cast<v4i*>(tw + w_ofs + 8 * DSA_IDX_DIM) = hi_half;
+    const v4i a = *reinterpret_cast<const v4i*>(tw + r_ofs);
+    const v4i c = *reinterpret_cast<const v4i*>(tw + r_ofs + 16);
+    return v8i{a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+  };
 #pragma unroll
-  for (int u = 0; u < NPF; ++u) {
-    pgr[u] = page_id(u);
-    const __amdgpu_buffer_rsrc_t kr = key_rsrc(pgr[u]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kf[u][c] = load_tile(kr, c);
-    ksr[u] = load_scale(pgr[u]);
-  }
+  for (int q = 0; q < QN; ++q) kr[q] = load_part(key_rsrc(page_id(q / 8)), q % 8);
+  ksr[0] = load_scale(page_id(0));
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  for (int i0 = 0; i0 < np; i0 += NPF) {
+  for (int i0 = 0; i0 < np; i0 += GP) {
 #pragma unroll
-    for (int u = 0; u < NPF; ++u) {
+    for (int u = 0; u < GP; ++u) {
       const int i = i0 + u;
-      const int pg = pgr[u];
-      const int nx = page_id(i + NPF);
-      const __amdgpu_buffer_rsrc_t nr = key_rsrc(nx);
-      // every wave runs whole groups of NPF pages; past np the pages are
+      const int pg = page_id(i);
+      // every wave runs whole groups of GP pages; past np the pages are
       // zero-size (their loads read nothing) and nothing is stored
       float part[RG][4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        // the tile's operand through LDS; its two ring registers then take
+        // the chunks QN ahead (the fences keep the loads after the LDS
+        // writes that read those registers, and the MFMAs after the loads,
+        // so the loads are in flight as early as possible)
+        const int q = 8 * u + 2 * c;  // chunk within the group (a multiple of QN starts it)
+        const v8i kb = transpose(kr[q % QN], kr[(q + 1) % QN]);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          const int qn = q + QN;
+          const __amdgpu_buffer_rsrc_t nr = key_rsrc(page_id(i0 + qn / 8));
+          kr[q % QN] = load_part(nr, qn % 8);
+          kr[(q + 1) % QN] = load_part(nr, (qn + 1) % 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         v4f acc[RG][4];
 #pragma unroll
         for (int r = 0; r < RG; ++r)
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            acc[r][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[r][m], kf[u][c], zero, 0,
+            acc[r][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[r][m], kb, zero, 0,
                                                                       0, 0, 0, 0, 0);
-        // the next page's tile c reuses this tile's registers: keep the
-        // scheduler from hoisting the loads above the MFMAs that read them
-        __builtin_amdgcn_sched_barrier(0);
-        kf[u][c] = load_tile(nr, c);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
@@ -383,6 +424,10 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
           for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sum = fmaf(wr[r][m][e], relu(acc[r][m][e]), sum);
+          // the empty asm pins the reduction here: left alone, the optimiser
+          // sinks it to the end of the page, which keeps the MFMA results of
+          // all four tiles live at once
+          asm volatile("" : "+v"(sum));
           part[r][c] = sum;
         }
         // one tile's MFMA results live at a time (the other waves of the
@@ -391,25 +436,32 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
       }
       const int lp = wave + kPageWaves * i;  // page within the work-group's range
       const int pos = (p_begin + lp) * DSA_PAGE_SIZE + lane;
+      // a page whose id is outside the pool holds no keys: its positions
+      // score -inf, below every real score
+      const bool ok = page_ok(pg);
+      const float ks = ksr[u];
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
         const float tot = reduce_scatter4(part[r]);
-        if (page_ok(pg) && r < n && pos < vis[r]) {
-          const float sc = tot * qs[r] * ksr[u];
+        if (i < np && r < n && pos < vis[r]) {
+          const float sc = ok ? tot * qs[r] * ks : -INFINITY;
           lsc[r][lp * DSA_PAGE_SIZE + lane] = sc;
-          if (HIST) atomicAdd(&lh[r * kTopkBins + (float_key(sc) >> 21)], 1u);
+          if (HIST) {
+            const uint32_t key = float_key(sc);
+            atomicAdd(&lh[r * (kTopkBins / 2) + (key >> 22)], 1u << (((key >> 21) & 1u) * 16));
+          }
         }
       }
-      ksr[u] = load_scale(nx);
-      pgr[u] = nx;
+      // the next page's key scales, one page ahead of their use
+      ksr[(u + 1) % GP] = load_scale(page_id(i + 1));
     }
   }
 
   __syncthreads();
-  // scores of the range, row by row: positions below the row's visible count
-  // on pages with a valid id, in 16-byte stores where the row is aligned.
-  // The stores are nontemporal: written while the key stream is being read,
-  // cached writes cost the scan far more than their share of the bytes.
+  // scores of the range, row by row: positions below the row's visible
+  // count, in 16-byte stores where the row is aligned.  The stores are
+  // nontemporal: written while the key stream is being read, cached writes
+  // cost the scan far more than their share of the bytes.
   const int base = p_begin * DSA_PAGE_SIZE;
   const int span = (p_end - p_begin) * DSA_PAGE_SIZE;
   for (int r = 0; r < n; ++r) {
@@ -417,7 +469,6 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
     float* row = scores + (int64_t)(c0 + r) * ld + base;
     const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
     for (int x = 4 * threadIdx.x; x < lim; x += 4 * kThreads) {
-      if (!page_ok(ptab[p_begin + x / DSA_PAGE_SIZE])) continue;
       if (vec && x + 4 <= lim) {
         __builtin_nontemporal_store(*reinterpret_cast<const v4f*>(&lsc[r][x]),
                                     reinterpret_cast<v4f*>(row + x));
@@ -427,28 +478,32 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
     }
   }
   if (HIST) {
-    for (int i = threadIdx.x; i < n * kTopkBins; i += kThreads) {
+    for (int i = threadIdx.x; i < n * (kTopkBins / 2); i += kThreads) {
       const uint32_t c = lh[i];
-      if (c) atomicAdd(&hist[(int64_t)(c0 + i / kTopkBins) * kTopkBins + (i % kTopkBins)], c);
+      if (c) {
+        uint32_t* gh = hist + (int64_t)(c0 + i / (kTopkBins / 2)) * kTopkBins + 2 * (i % (kTopkBins / 2));
+        if (c & 0xffffu) atomicAdd(gh, c & 0xffffu);
+        if (c >> 16) atomicAdd(gh + 1, c >> 16);
+      }
     }
   }
 }
 
-template <int RG, int NPF, int STAGE>
+template <int RG, int QN, int STAGE>
 hipError_t launch_page(int chunk_pages, int chunks, hipStream_t s, const BatchArgs& b,
                        const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
                        const float* k_scale, float* scores, int64_t ld, uint32_t* hist) {
   const dim3 grid(chunks, b.B);
   if (hist)
-    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, true, STAGE>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((index_score_page_kernel<RG, QN, true, STAGE>), grid, dim3(kThreads), 0,
                        s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
   else
-    hipLaunchKernelGGL((index_score_page_kernel<RG, NPF, false, STAGE>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((index_score_page_kernel<RG, QN, false, STAGE>), grid, dim3(kThreads), 0,
                        s, b, q8, q_scale, w, k8, k_scale, scores, ld, hist, chunk_pages);
   return hipGetLastError();
 }
 
-template <int RG, int NPF>
+template <int RG, int QN>
 hipError_t launch_page_sized(bool shared, int total_pages, hipStream_t s, const BatchArgs& b,
                              const uint8_t* q8, const float* q_scale, const float* w,
                              const uint8_t* k8, const float* k_scale, float* scores, int64_t ld,
@@ -462,9 +517,9 @@ hipError_t launch_page_sized(bool shared, int total_pages, hipStream_t s, const 
   cp = std::max(kPageWaves, (cp + kPageWaves - 1) / kPageWaves * kPageWaves);
   const int chunks = (total_pages + cp - 1) / cp;
   if (shared)
-    return launch_page<RG, NPF, kSharedStagePages>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale,
+    return launch_page<RG, QN, kSharedStagePages>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale,
                                                    scores, ld, hist);
-  return launch_page<RG, NPF, kStagePages>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores,
+  return launch_page<RG, QN, kStagePages>(cp, chunks, s, b, q8, q_scale, w, k8, k_scale, scores,
                                            ld, hist);
 }
 
@@ -478,9 +533,9 @@ hipError_t launch_index_score(const BatchArgs& b, const uint8_t* q8, const float
   const int total_pages = (b.max_seqlen_k + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE;
   if (b.max_q <= 2) {
     if (b.max_q <= 1)
-      return launch_page_sized<1, kScanNPF1>(shared, total_pages, s, b, q8, q_scale, w, k8,
+      return launch_page_sized<1, kScanQN1>(shared, total_pages, s, b, q8, q_scale, w, k8,
                                              k_scale, scores, ld, hist);
-    return launch_page_sized<2, kScanNPF2>(shared, total_pages, s, b, q8, q_scale, w, k8, k_scale,
+    return launch_page_sized<2, kScanQN2>(shared, total_pages, s, b, q8, q_scale, w, k8, k_scale,
                                            scores, ld, hist);
   }
   const int groups = (b.max_q + 3) / 4;

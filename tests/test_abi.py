@@ -220,6 +220,31 @@ def test_decode_step_argument_checks(L):
         B.DSA_ERR_WORKSPACE
 
 
+def test_mli_step_refuses_attend_idx_overlapping_idx_out(L):
+    """In MLI mode the aux stream's top-k writes idx_out while the main
+    stream's attention reads attend_idx: overlapping ranges are refused
+    before anything is enqueued; disjoint ones pass the check (the call then
+    fails later only on the workspace size given here)."""
+    P = 0x10000
+    b = _batch()  # T = 4
+    k = 64
+    span = 4 * k * 4  # T * k int32
+    ix = B.dsa_indexer_inputs_t(P, P, P, P, P)
+    ml = B.dsa_mla_inputs_t(P, P, 0.07)
+    need = L.dsa_workspace_size(B.DSA_OP_DECODE_STEP, ctypes.byref(b), k, 0)
+    idx_out = 0x200000
+    for attend, overlapping in ((idx_out, True), (idx_out + span - 4, True),
+                                (idx_out - span + 4, True), (idx_out + span, False),
+                                (idx_out - span, False)):
+        mli = B.dsa_step_opts_t(B.DSA_MODE_MLI, 0, attend)
+        rc = L.dsa_decode_step(ctypes.byref(b), ctypes.byref(ix), ctypes.byref(ml), k,
+                               ctypes.byref(mli), idx_out, P, None, P, need - 1, 0x2000, 0x3000)
+        if overlapping:
+            assert rc == B.DSA_ERR_INVALID_ARG and "overlaps" in _err(L), (hex(attend), rc)
+        else:
+            assert rc == B.DSA_ERR_WORKSPACE, (hex(attend), rc, _err(L))
+
+
 def test_empty_batch_is_a_no_op(L):
     b = B.dsa_batch_t(0, 0, 0, 0, 0, 0, None, None, None)
     assert L.dsa_topk(ctypes.byref(b), None, 0, 16, None, None, 0, None) == B.DSA_OK
