@@ -271,10 +271,15 @@ typedef struct {
   void* const* stage_events;
 } dsa_step_opts_t;
 
-/* One decode step of one layer: indexer scores, top-k, sparse MLA.  When
- * max_seqlen_k <= k every row keeps all its visible tokens, so the step
- * writes that selection without scanning and attends densely (same results
- * as the scan would give).
+/* One decode step of one layer: indexer scores, top-k, sparse MLA -- the
+ * three parts of the DSA bullet of "MTP and sparse attention: NSA and DSA"
+ * run back to back for a batch laid out as "[SGLang] NSA" describes it
+ * (init_forward_metadata: 1 + MTP query rows per request, cached lengths
+ * that include them, cumulative query offsets, a 64-token page table), with
+ * the attention's KV splits merged by log-sum-exp as in "Deepseek Details",
+ * section DSA, stages 2-3.  When max_seqlen_k <= k every row keeps all its
+ * visible tokens, so the step writes that selection without scanning and
+ * attends densely (same results as the scan would give).
  *  ix, mla   this layer's inputs
  *  k         tokens kept per row
  *  idx_out   int32 [T, k] out: the selection of ix (as dsa_topk)
@@ -290,6 +295,25 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
                     const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
                     int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                     void* stream_main, void* stream_aux);
+
+/* dsa_decode_step for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid allocation.  It takes no workspace: the step runs in a static
+ * scratch array of 64 MiB that the library keeps in each device's memory
+ * for the life of the process (the first call on a device resolves that
+ * device's copy; make it outside graph capture).  It calls no allocator.
+ * Arguments and results as dsa_decode_step, in FUSED mode only (opts->mode
+ * must be DSA_MODE_FUSED; opts->n_split and opts->stage_events as there).
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap on one device (different streams, different threads) race.  The
+ * scratch keeps the last call's contents; the step clears what it needs
+ * cleared itself.
+ * Errors: as dsa_decode_step; WORKSPACE (nothing enqueued) when the batch's
+ * step needs more than 64 MiB, i.e. more than
+ * dsa_workspace_size(DSA_OP_DECODE_STEP, batch, k, n_split) allows. */
+int dsa_decode_step_noalloc(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
+                            const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
+                            int32_t* idx_out, uint16_t* out, float* lse, void* stream);
 
 /* One layer of a multi-layer decode (device pointers, layouts as above). */
 typedef struct {

@@ -22,7 +22,7 @@ PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 12
 
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
            "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
-           "dsa_decode_layers", "dsa_dense_mla_decode",
+           "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc",
            "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
 
 
@@ -86,9 +86,12 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_layers.argtypes = [bp, i32, ctypes.POINTER(dsa_layer_t), i32, i32, i32, i32,
                                         vp, vp, sz, vp, vp]
         L.dsa_dense_mla_decode.argtypes = [bp, vp, vp, f32, vp, vp, i32, vp, sz, vp]
+        L.dsa_decode_step_noalloc.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
+                                              ctypes.POINTER(dsa_mla_inputs_t), i32,
+                                              ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp]
         for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
                   "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
-                  "dsa_decode_layers", "dsa_dense_mla_decode"):
+                  "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
         L.dsa_workspace_size.restype = sz
@@ -219,6 +222,24 @@ def dsa_decode_step(batch: Batch, ix: dict, mla: dict, k: int, mode: int, n_spli
     _check(lib().dsa_decode_step(batch.ref(), ctypes.byref(ixs), ctypes.byref(ms), int(k),
                                  ctypes.byref(opts), _ptr(idx_out), _ptr(out), _ptr(lse),
                                  _ptr(ws), int(ws_bytes), _stream(stream_main), aux))
+
+
+def dsa_decode_step_noalloc(batch: Batch, ix: dict, mla: dict, k: int, n_split: int, idx_out, out,
+                            lse, stream=None, stage_events=None):
+    """dsa_decode_step (FUSED) in the library's static scratch: no workspace."""
+    evs = None
+    if stage_events is not None:
+        if len(stage_events) != 2 * DSA_NUM_STAGES or not all(stage_events):
+            raise ValueError(f"stage_events needs {2 * DSA_NUM_STAGES} event handles")
+        evs = (ctypes.c_void_p * len(stage_events))(*stage_events)
+    ixs = dsa_indexer_inputs_t(_ptr(ix["q8"]), _ptr(ix["q_scale"]), _ptr(ix["w"]),
+                               _ptr(ix["k8_cache"]), _ptr(ix["k_scale"]))
+    ms = dsa_mla_inputs_t(_ptr(mla["q"]), _ptr(mla["kv_cache"]), float(mla["sm_scale"]))
+    opts = dsa_step_opts_t(DSA_MODE_FUSED, int(n_split), None,
+                           None if evs is None else ctypes.cast(evs, ctypes.c_void_p))
+    _check(lib().dsa_decode_step_noalloc(batch.ref(), ctypes.byref(ixs), ctypes.byref(ms), int(k),
+                                         ctypes.byref(opts), _ptr(idx_out), _ptr(out), _ptr(lse),
+                                         _stream(stream)))
 
 
 def dsa_decode_layers(batch: Batch, layers: list, k: int, retention: int, mli: int, n_split: int,

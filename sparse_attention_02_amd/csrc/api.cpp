@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dsa.h"
@@ -122,6 +123,48 @@ int get_events(hipEvent_t* start, hipEvent_t* done) {
   *done = g_events.done;
   return DSA_OK;
 }
+
+// ---- static scratch of dsa_decode_step_noalloc ------------------------------
+// The workspace of the step for callers that cannot allocate: one array in
+// each device's memory for the life of the process.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol); it asks the runtime for the device address once per device and
+// passes that pointer to the kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of this device's scratch (resolved on the first call with
+// the device current).
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "device ordinal beyond the static scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+int decode_step_impl(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
+                     const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
+                     int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream_main, void* stream_aux);
 
 }  // namespace
 
@@ -365,6 +408,47 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
                     int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                     void* stream_main, void* stream_aux) {
   g_err.clear();
+  return decode_step_impl(batch, ix, mla, k, opts, idx_out, out, lse, ws, ws_bytes, stream_main,
+                          stream_aux);
+}
+
+int dsa_decode_step_noalloc(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
+                            const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
+                            int32_t* idx_out, uint16_t* out, float* lse, void* stream) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (!opts) return fail(DSA_ERR_INVALID_ARG, "NULL argument struct");
+  if (opts->mode != DSA_MODE_FUSED)
+    return fail(DSA_ERR_INVALID_ARG, "dsa_decode_step_noalloc runs FUSED steps only");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  int used = 1;
+  rc = resolve_splits(batch, k, opts->n_split, &used);
+  if (rc) return rc;
+  if (batch->num_tokens == 0) return DSA_OK;
+  const size_t need = step_layout(batch, used).total;
+  if (need > kScratchBytes) {
+    char msg[160];
+    snprintf(msg, sizeof msg,
+             "the step needs %zu bytes of workspace; the static scratch holds 64 MiB "
+             "(use dsa_decode_step with a caller workspace)", need);
+    return fail(DSA_ERR_WORKSPACE, msg);
+  }
+  void* ws = nullptr;
+  rc = scratch_on_device(&ws);
+  if (rc) return rc;
+  return decode_step_impl(batch, ix, mla, k, opts, idx_out, out, lse, ws, kScratchBytes, stream,
+                          nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_step_impl(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
+                     const dsa_mla_inputs_t* mla, int32_t k, const dsa_step_opts_t* opts,
+                     int32_t* idx_out, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream_main, void* stream_aux) {
   int rc = check_batch(batch);
   if (rc) return rc;
   if (!ix || !mla || !opts) return fail(DSA_ERR_INVALID_ARG, "NULL argument struct");
@@ -488,4 +572,4 @@ int dsa_decode_step(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
   return DSA_OK;
 }
 
-}  // extern "C"
+}  // namespace

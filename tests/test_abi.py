@@ -245,6 +245,31 @@ def test_mli_step_refuses_attend_idx_overlapping_idx_out(L):
             assert rc == B.DSA_ERR_WORKSPACE, (hex(attend), rc, _err(L))
 
 
+def test_noalloc_step_argument_checks(L):
+    """The static-scratch step runs FUSED steps only and refuses, before any
+    device call, a batch whose step needs more than its 64 MiB."""
+    P = 0x10000
+    ix = B.dsa_indexer_inputs_t(P, P, P, P, P)
+    ml = B.dsa_mla_inputs_t(P, P, 0.07)
+    fused = B.dsa_step_opts_t(B.DSA_MODE_FUSED, 0, None)
+    mli = B.dsa_step_opts_t(B.DSA_MODE_MLI, 0, P)
+    small = _batch()
+    assert L.dsa_decode_step_noalloc(ctypes.byref(small), ctypes.byref(ix), ctypes.byref(ml), 64,
+                                     ctypes.byref(mli), P, P, None, None) == B.DSA_ERR_INVALID_ARG
+    assert "FUSED" in _err(L)
+    assert L.dsa_decode_step_noalloc(ctypes.byref(small), ctypes.byref(ix), ctypes.byref(ml), 64,
+                                     None, P, P, None, None) == B.DSA_ERR_INVALID_ARG
+    big = B.dsa_batch_t(64, 128, 2, 131072, 2048, 131072, P, P, P)
+    need = L.dsa_workspace_size(B.DSA_OP_DECODE_STEP, ctypes.byref(big), 2048, 0)
+    assert need > 64 << 20
+    assert L.dsa_decode_step_noalloc(ctypes.byref(big), ctypes.byref(ix), ctypes.byref(ml), 2048,
+                                     ctypes.byref(fused), P, P, None, None) == B.DSA_ERR_WORKSPACE
+    assert "64 MiB" in _err(L)
+    empty = B.dsa_batch_t(0, 0, 0, 0, 0, 0, None, None, None)
+    assert L.dsa_decode_step_noalloc(ctypes.byref(empty), ctypes.byref(ix), ctypes.byref(ml), 64,
+                                     ctypes.byref(fused), None, None, None, None) == B.DSA_OK
+
+
 def test_empty_batch_is_a_no_op(L):
     b = B.dsa_batch_t(0, 0, 0, 0, 0, 0, None, None, None)
     assert L.dsa_topk(ctypes.byref(b), None, 0, 16, None, None, 0, None) == B.DSA_OK
