@@ -60,7 +60,9 @@ typedef enum {
   DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent scalars */
   DSA_ERR_UNSUPPORTED = 2, /* a shape outside what the kernels implement */
   DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dsa_workspace_size() */
-  DSA_ERR_HIP = 4          /* a HIP launch or event call failed */
+  DSA_ERR_HIP = 4,         /* a HIP launch or event call failed */
+  DSA_ERR_DEVICE_CHECK = 5 /* checked builds: a kernel found bad device data
+                            * (reported by dsa_device_check) */
 } dsa_status;
 
 /* One batch of requests (host struct; the arrays it points to are on the device).
@@ -362,6 +364,34 @@ size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n
 /* KV splits the library chooses for a batch when n_split = 0 (the single
  * ops and FUSED steps; MLI steps choose at most this many). */
 int32_t dsa_default_splits(const dsa_batch_t* batch, int32_t k);
+
+/* Device checks.  The library is also built as libdsa_checked.so, compiled
+ * with DSA_DEVICE_CHECKS: there its kernels test the device data they are
+ * handed against the batch's host scalars and record what they find in a
+ * device word (one per device, flags ORed by vector atomics), without
+ * changing what they compute.  The page tables checked are those of
+ * "[SGLang] NSA" (NSAMetadata); the index entries those the top-k hands the
+ * sparse kernel.  Flags: */
+#define DSA_CHECK_PAGE_ID 1u   /* a visible position (or a new token's slot)
+                                  maps to a page id outside [0, num_pages) */
+#define DSA_CHECK_INDEX 2u     /* an attention index entry below -1, at or past
+                                  its row's visible length, or a slot outside
+                                  the pool */
+#define DSA_CHECK_NAN_SCORE 4u /* an indexer score, or a score given to the
+                                  top-k, is NaN (normal builds rank NaN above
+                                  +inf) */
+#define DSA_CHECK_METADATA 8u  /* a request's cached length outside
+                                  [0, max_seqlen_k], or its row count above
+                                  max_q */
+/* Reads and clears this device's check word.  Call it after the work to be
+ * checked has finished (it synchronises `stream` itself before reading).
+ * flags_out (may be NULL) receives the flags.  Returns DSA_ERR_DEVICE_CHECK
+ * when any flag was set, DSA_OK otherwise; in normal builds the checks are
+ * compiled out and it returns DSA_OK with 0.  Errors: HIP. */
+int dsa_device_check(uint32_t* flags_out, void* stream);
+
+/* 1 in libdsa_checked.so, 0 in libdsa.so. */
+int32_t dsa_device_checks_enabled(void);
 
 const char* dsa_status_string(int status);
 

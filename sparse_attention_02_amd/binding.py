@@ -6,14 +6,25 @@ the path runs in the library's HIP kernels; there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# libdsa_checked.so: the same kernels compiled with device checks (bad page
+# ids, index entries, NaN scores and metadata are recorded in a device word
+# that dsa_device_check reports).  DSA_DEVICE_CHECKS=1 in the environment
+# makes lib() load it instead of libdsa.so.
+_LIB_CHECKED_PATH = os.path.join(_HERE, "libdsa_checked.so")
+if os.environ.get("DSA_DEVICE_CHECKS", "0") not in ("", "0"):
+    _LIB_PATH = _LIB_CHECKED_PATH
 
-DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+(DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP,
+ DSA_ERR_DEVICE_CHECK) = range(6)
+DSA_CHECK_PAGE_ID, DSA_CHECK_INDEX, DSA_CHECK_NAN_SCORE, DSA_CHECK_METADATA = 1, 2, 4, 8
 DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP, DSA_OP_DENSE_MLA = 1, 2, 3, 4
 DSA_MODE_FUSED, DSA_MODE_MLI = 0, 1
 DSA_STAGE_INDEX_SCORE, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_NUM_STAGES = 0, 1, 2, 3
@@ -23,7 +34,8 @@ PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 12
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
            "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
            "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc",
-           "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error"]
+           "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error",
+           "dsa_device_check", "dsa_device_checks_enabled"]
 
 
 class DsaError(RuntimeError):
@@ -61,48 +73,73 @@ class dsa_step_opts_t(ctypes.Structure):
 
 
 _lib = None
+_loaded = {}
 
 
 def lib() -> ctypes.CDLL:
-    """Load libdsa.so; raises if it has not been built."""
+    """Load libdsa.so (or libdsa_checked.so, see above); raises if it has not
+    been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
-                               "`python -c 'import __graft_entry__ as g; g.build()'`")
-        L = ctypes.CDLL(_LIB_PATH)
-        vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
-                                 ctypes.c_float)
-        bp = ctypes.POINTER(dsa_batch_t)
-        L.dsa_index_score.argtypes = [bp, vp, vp, vp, vp, vp, vp, i64, vp]
-        L.dsa_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
-        L.dsa_sparse_mla_decode.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
-        L.dsa_decode_step.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
-                                      ctypes.POINTER(dsa_mla_inputs_t), i32,
-                                      ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp, sz, vp, vp]
-        L.dsa_cache_append.argtypes = [bp, vp, vp, vp, vp, vp, vp]
-        L.dsa_topk_transform.argtypes = [bp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
-        L.dsa_sparse_mla_decode_paged.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
-        L.dsa_decode_layers.argtypes = [bp, i32, ctypes.POINTER(dsa_layer_t), i32, i32, i32, i32,
-                                        vp, vp, sz, vp, vp]
-        L.dsa_dense_mla_decode.argtypes = [bp, vp, vp, f32, vp, vp, i32, vp, sz, vp]
-        L.dsa_decode_step_noalloc.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
-                                              ctypes.POINTER(dsa_mla_inputs_t), i32,
-                                              ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp]
-        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
-                  "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
-                  "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc"):
-            getattr(L, f).restype = ctypes.c_int
-        L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
-        L.dsa_workspace_size.restype = sz
-        L.dsa_default_splits.argtypes = [bp, i32]
-        L.dsa_default_splits.restype = i32
-        L.dsa_status_string.argtypes = [ctypes.c_int]
-        L.dsa_status_string.restype = ctypes.c_char_p
-        L.dsa_last_error.argtypes = []
-        L.dsa_last_error.restype = ctypes.c_char_p
-        _lib = L
+        _lib = _load(_LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def checked():
+    """Within the block every call goes to libdsa_checked.so."""
+    global _lib
+    prev = lib()
+    _lib = _load(_LIB_CHECKED_PATH)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                             ctypes.c_float)
+    bp = ctypes.POINTER(dsa_batch_t)
+    L.dsa_index_score.argtypes = [bp, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.dsa_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
+    L.dsa_sparse_mla_decode.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
+    L.dsa_decode_step.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
+                                  ctypes.POINTER(dsa_mla_inputs_t), i32,
+                                  ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp, sz, vp, vp]
+    L.dsa_cache_append.argtypes = [bp, vp, vp, vp, vp, vp, vp]
+    L.dsa_topk_transform.argtypes = [bp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_decode_paged.argtypes = [bp, vp, vp, vp, i32, f32, vp, vp, i32, vp, sz, vp]
+    L.dsa_decode_layers.argtypes = [bp, i32, ctypes.POINTER(dsa_layer_t), i32, i32, i32, i32,
+                                    vp, vp, sz, vp, vp]
+    L.dsa_dense_mla_decode.argtypes = [bp, vp, vp, f32, vp, vp, i32, vp, sz, vp]
+    L.dsa_decode_step_noalloc.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
+                                          ctypes.POINTER(dsa_mla_inputs_t), i32,
+                                          ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp]
+    for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
+              "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
+              "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc"):
+        getattr(L, f).restype = ctypes.c_int
+    L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
+    L.dsa_workspace_size.restype = sz
+    L.dsa_default_splits.argtypes = [bp, i32]
+    L.dsa_default_splits.restype = i32
+    L.dsa_status_string.argtypes = [ctypes.c_int]
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_last_error.argtypes = []
+    L.dsa_last_error.restype = ctypes.c_char_p
+    L.dsa_device_check.argtypes = [ctypes.POINTER(ctypes.c_uint32), vp]
+    L.dsa_device_check.restype = ctypes.c_int
+    L.dsa_device_checks_enabled.argtypes = []
+    L.dsa_device_checks_enabled.restype = i32
+    _loaded[path] = L
+    return L
 
 
 def _ptr(t) -> int | None:
@@ -148,6 +185,20 @@ class Batch:
 
     def ref(self):
         return ctypes.byref(self.c)
+
+
+def dsa_device_check(stream=None) -> int:
+    """Reads and clears the device check word (synchronising the stream);
+    returns its DSA_CHECK_* flags (0 in normal builds)."""
+    flags = ctypes.c_uint32(0)
+    rc = lib().dsa_device_check(ctypes.byref(flags), _stream(stream))
+    if rc not in (DSA_OK, DSA_ERR_DEVICE_CHECK):
+        _check(rc)
+    return int(flags.value)
+
+
+def dsa_device_checks_enabled() -> bool:
+    return bool(lib().dsa_device_checks_enabled())
 
 
 def dsa_workspace_size(op: int, batch: Batch, k: int, n_split: int = 0) -> int:

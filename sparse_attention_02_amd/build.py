@@ -1,4 +1,6 @@
-"""Build libdsa.so (the C-ABI library with its gfx950 HIP kernels) in-tree."""
+"""Build libdsa.so (the C-ABI library with its gfx950 HIP kernels) in-tree, and
+libdsa_checked.so, the same sources compiled with DSA_DEVICE_CHECKS (kernels
+record bad device data in a check word that dsa_device_check reports)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
+LIB_CHECKED = os.path.join(PKG, "libdsa_checked.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip"]
 # per-file code-generation options: the indexer reads its MFMA results with
 # VALU right away, so they are kept in VGPRs instead of AGPRs
@@ -46,8 +49,8 @@ def _run(cmd, verbose):
         raise RuntimeError("hipcc failed building libdsa.so")
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every source for gfx950 (one object each) and link libdsa.so."""
+def build_one(out: str, verbose: bool = False, extra=()) -> str:
+    """Compile every source for gfx950 (one object each) and link `out`."""
     import tempfile
     with tempfile.TemporaryDirectory(prefix="dsa_build_") as tmpdir:
         objs = []
@@ -56,10 +59,20 @@ def build(verbose: bool = False, extra=()) -> str:
             _run(["hipcc", *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC,
                   "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
             objs.append(obj)
-        tmp = LIB + ".tmp"
+        tmp = out + ".tmp"
         _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Build libdsa.so and libdsa_checked.so; returns the path of libdsa.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        a = ex.submit(build_one, LIB, verbose, tuple(extra))
+        c = ex.submit(build_one, LIB_CHECKED, verbose, tuple(extra) + ("-DDSA_DEVICE_CHECKS=1",))
+        c.result()
+        return a.result()
 
 
 if __name__ == "__main__":

@@ -139,7 +139,42 @@ void* g_scratch_ptr[kScratchDevices] = {};
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
+#ifdef DSA_DEVICE_CHECKS
+// flags the checked kernels record (DSA_CHECK_*), one word per device
+static __device__ uint32_t check_word;
+#endif
+
 namespace {
+
+#ifdef DSA_DEVICE_CHECKS
+std::mutex g_check_mu;
+uint32_t* g_check_ptr[kScratchDevices] = {};
+#endif
+
+// Device address of this device's check word (NULL in normal builds, or if
+// it cannot be resolved: the query call then reports the error).
+uint32_t* check_word_ptr() {
+#ifdef DSA_DEVICE_CHECKS
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_check_mu);
+  if (!g_check_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(check_word)) != hipSuccess) return nullptr;
+    g_check_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  return g_check_ptr[dev];
+#else
+  return nullptr;
+#endif
+}
+
+// The batch's device view for a launch (with the check word in checked builds).
+BatchArgs launch_args(const dsa_batch_t& b) {
+  BatchArgs a = dsa::batch_args(b);
+  a.check = check_word_ptr();
+  return a;
+}
 
 // Device address of this device's scratch (resolved on the first call with
 // the device current).
@@ -177,11 +212,47 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "unsupported shape";
     case DSA_ERR_WORKSPACE: return "workspace too small";
     case DSA_ERR_HIP: return "HIP error";
+    case DSA_ERR_DEVICE_CHECK: return "device check failed";
     default: return "unknown status";
   }
 }
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int32_t dsa_device_checks_enabled(void) {
+#ifdef DSA_DEVICE_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+int dsa_device_check(uint32_t* flags_out, void* stream) {
+  g_err.clear();
+  if (flags_out) *flags_out = 0;
+#ifdef DSA_DEVICE_CHECKS
+  uint32_t* p = check_word_ptr();
+  if (!p) return fail(DSA_ERR_HIP, "cannot resolve the device check word");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t flags = 0;
+  e = hipMemcpy(&flags, p, sizeof flags, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (check word)");
+  if (flags) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy (check word reset)");
+    char msg[96];
+    snprintf(msg, sizeof msg, "device checks found bad data (flags 0x%x)", flags);
+    g_err = msg;
+  }
+  if (flags_out) *flags_out = flags;
+  return flags ? DSA_ERR_DEVICE_CHECK : DSA_OK;
+#else
+  (void)stream;
+  return DSA_OK;
+#endif
+}
 
 int32_t dsa_default_splits(const dsa_batch_t* batch, int32_t k) {
   if (check_batch(batch) != DSA_OK || k < 1) return 1;
@@ -223,7 +294,7 @@ int dsa_decode_layers(const dsa_batch_t* batch, int32_t n_layers, const dsa_laye
   const StepWs W = step_layout(batch, used);
   if (ws_bytes < W.total || !ws) return fail(DSA_ERR_WORKSPACE, "step workspace too small");
 
-  const dsa::BatchArgs a = dsa::batch_args(*batch);
+  const dsa::BatchArgs a = launch_args(*batch);
   const int64_t per = (int64_t)batch->num_tokens * k;
   void* mla_ws = static_cast<char*>(ws) + W.mla_off;
   for (int32_t l = 0; l < n_layers; ++l) {
@@ -288,7 +359,7 @@ int dsa_index_score(const dsa_batch_t* batch, const uint8_t* q8, const float* q_
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   rc = check_index_align(q8, k8_cache, scores);
   if (rc) return rc;
-  hipError_t e = dsa::launch_index_score(dsa::batch_args(*batch), q8, q_scale, w, k8_cache,
+  hipError_t e = dsa::launch_index_score(launch_args(*batch), q8, q_scale, w, k8_cache,
                                          k_scale, scores, ld, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "index_score launch");
 }
@@ -306,7 +377,7 @@ int dsa_cache_append(const dsa_batch_t* batch, const uint16_t* k_new, const uint
       misaligned(k8_cache, 2) || misaligned(k_scale, 4))
     return fail(DSA_ERR_INVALID_ARG,
                 "kv_new / kv_cache need 16-byte, k_new / k_scale 4-byte, k8_cache 2-byte alignment");
-  hipError_t e = dsa::launch_cache_append(dsa::batch_args(*batch), k_new, kv_new, k8_cache, k_scale,
+  hipError_t e = dsa::launch_cache_append(launch_args(*batch), k_new, kv_new, k8_cache, k_scale,
                                           kv_cache, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "cache_append launch");
 }
@@ -332,7 +403,7 @@ int topk_common(const dsa_batch_t* batch, const float* scores, int64_t ld, int32
   const size_t need = dsa::topk_ws_layout(dsa::batch_args(*batch)).total;
   if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "top-k workspace too small");
   if (misaligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws needs 16-byte alignment");
-  hipError_t e = dsa::launch_topk(dsa::batch_args(*batch), scores, ld, k, idx, ws,
+  hipError_t e = dsa::launch_topk(launch_args(*batch), scores, ld, k, idx, ws,
                                   (hipStream_t)stream, space, kv_offsets);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");
 }
@@ -359,7 +430,7 @@ int mla_common(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_c
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   rc = check_mla_align(q, kv_cache, out, ws);
   if (rc) return rc;
-  const dsa::BatchArgs a = dsa::batch_args(*batch);
+  const dsa::BatchArgs a = launch_args(*batch);
   const size_t need = dsa::mla_ws_layout(a, used).total;
   if (need > 0 && (ws_bytes < need || !ws))
     return fail(DSA_ERR_WORKSPACE, "attention workspace too small");
@@ -483,7 +554,7 @@ int decode_step_impl(const dsa_batch_t* batch, const dsa_indexer_inputs_t* ix,
     return fail(DSA_ERR_UNSUPPORTED, "rows longer than 393216 tokens need k <= 4096");
   const StepWs L = step_layout(batch, used);
   if (ws_bytes < L.total || !ws) return fail(DSA_ERR_WORKSPACE, "step workspace too small");
-  const BatchArgs a = dsa::batch_args(*batch);
+  const BatchArgs a = launch_args(*batch);
   char* base = static_cast<char*>(ws);
   float* scores = reinterpret_cast<float*>(base + L.scores_off);
   void* topk_ws = base + L.topk_off;

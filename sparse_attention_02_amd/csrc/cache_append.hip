@@ -34,8 +34,11 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
   const int bi = row_request(b.cu, b.B, t);
   const int n = b.cu[bi + 1] - b.cu[bi];
   const int pos = clamp_len(b, b.lens[bi]) - n + (t - b.cu[bi]);
-  if (pos < 0) return;  // a request whose cached length does not hold its rows
+  // a request whose cached length does not hold its rows
+  device_check(b, pos < 0, DSA_CHECK_METADATA);
+  if (pos < 0) return;
   const int64_t slot = slot_of(b, bi, pos);
+  device_check(b, slot < 0, DSA_CHECK_PAGE_ID);
   if (slot < 0) return;  // page id outside the pool: nothing is written
 
   const uint32_t kb = reinterpret_cast<const uint32_t*>(k_new + (int64_t)t * DSA_IDX_DIM)[lane];

@@ -12,6 +12,18 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// Records `flag` in the device check word when `bad` holds (builds with
+// DSA_DEVICE_CHECKS; compiled out otherwise).  A vector atomic OR.
+__device__ __forceinline__ void device_check(const BatchArgs& b, bool bad, uint32_t flag) {
+#ifdef DSA_DEVICE_CHECKS
+  if (bad && b.check) atomicOr(b.check, flag);
+#else
+  (void)b;
+  (void)bad;
+  (void)flag;
+#endif
+}
+
 // Request owning query row t: the largest b with cu[b] <= t (rows of a
 // request with no rows are skipped because cu[b] == cu[b+1]).
 __device__ __forceinline__ int row_request(const int32_t* cu, int B, int t) {
@@ -30,6 +42,7 @@ __device__ __forceinline__ int clamp_len(const BatchArgs& b, int L) {
   int cap = b.max_seqlen_k;
   int pcap = b.max_pages * DSA_PAGE_SIZE;
   if (pcap < cap) cap = pcap;
+  device_check(b, L < 0 || L > cap, DSA_CHECK_METADATA);
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
@@ -37,6 +50,7 @@ __device__ __forceinline__ int clamp_len(const BatchArgs& b, int L) {
 __device__ __forceinline__ int row_visible(const BatchArgs& b, int bi, int t) {
   int c0 = b.cu[bi];
   int n = b.cu[bi + 1] - c0;
+  device_check(b, n > b.max_q, DSA_CHECK_METADATA);
   int L = clamp_len(b, b.lens[bi]);
   int v = L - n + 1 + (t - c0);
   return v < 0 ? 0 : (v > L ? L : v);

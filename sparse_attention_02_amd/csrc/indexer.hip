@@ -201,7 +201,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const int s = (p_begin + i) * DSA_PAGE_SIZE + 16 * wave + j;
     if (p_begin + i < p_end && g < nr && s < vis_g) {
       // a page whose id is outside the pool holds no keys: -inf
-      const float sc = page_ok(page_id(i)) ? mine * qs_g * kscur : -INFINITY;
+      const bool ok = page_ok(page_id(i));
+      device_check(b, !ok, DSA_CHECK_PAGE_ID);
+      const float sc = ok ? mine * qs_g * kscur : -INFINITY;
+      device_check(b, sc != sc, DSA_CHECK_NAN_SCORE);
       srow[s] = sc;
       if (HIST) atomicAdd(&lh[g * kTopkBins + (float_key(sc) >> 21)], 1u);
     }
@@ -296,6 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
   const int bi = blockIdx.y;
   const int c0 = b.cu[bi];
   const int n = b.cu[bi + 1] - c0;  // 0 .. RG rows (the launch checks max_q <= RG)
+  device_check(b, n < 0 || n > RG, DSA_CHECK_METADATA);
   if (n <= 0 || n > RG) return;
   const int L = clamp_len(b, b.lens[bi]);
   const int p_begin = chunk * chunk_pages;
@@ -439,12 +443,14 @@ __global__ __launch_bounds__(kThreads, 2) void index_score_page_kernel(
       // a page whose id is outside the pool holds no keys: its positions
       // score -inf, below every real score
       const bool ok = page_ok(pg);
+      device_check(b, i < np && !ok, DSA_CHECK_PAGE_ID);
       const float ks = ksr[u];
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
         const float tot = reduce_scatter4(part[r]);
         if (i < np && r < n && pos < vis[r]) {
           const float sc = ok ? tot * qs[r] * ks : -INFINITY;
+          device_check(b, sc != sc, DSA_CHECK_NAN_SCORE);
           lsc[r][lp * DSA_PAGE_SIZE + lane] = sc;
           if (HIST) {
             const uint32_t key = float_key(sc);

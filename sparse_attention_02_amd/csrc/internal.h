@@ -18,16 +18,17 @@ struct BatchArgs {
   const int32_t* cu;     // [B+1]
   const int32_t* lens;   // [B]
   const int32_t* pages;  // [B, max_pages]
+  uint32_t* check;       // device check word (builds with DSA_DEVICE_CHECKS), else NULL
 };
 
 inline BatchArgs batch_args(const dsa_batch_t& b) {
   return BatchArgs{b.batch,        b.num_tokens,   b.max_q,     b.max_seqlen_k,
                    b.max_pages_per_req, b.num_pages, b.cu_seqlens_q, b.seqlens_k,
-                   b.page_table};
+                   b.page_table, nullptr};
 }
 
 constexpr int kTopkBins = 2048;      // first radix digit: key bits 31..21
-constexpr int kTopkSeg = 8192;       // scores per histogram / collect work-group
+constexpr int kTopkSeg = 8192;       // scores per work-group of the standalone histogram pass
 constexpr int kMlaTile = 32;         // selected tokens per attention tile
 constexpr int kMaxSplits = 64;
 

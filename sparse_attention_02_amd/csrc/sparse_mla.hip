@@ -194,10 +194,14 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     if (i < ntok) {
       const int s = idx_mode == kMlaDense ? j0 + i : idx[(int64_t)t * k + j0 + i];
       if (idx_mode == kMlaPaged) {
+        device_check(b, s < -1 || s >= n_slots, DSA_CHECK_INDEX);
         if (s >= 0 && s < n_slots) slot = s;
       } else if (s >= 0 && s < v) {
         const int64_t sl = slot_of(b, bi, s);
+        device_check(b, sl < 0, DSA_CHECK_PAGE_ID);
         if (sl >= 0) slot = (int)sl;
+      } else {
+        device_check(b, s != -1, DSA_CHECK_INDEX);
       }
     }
     slots[i] = slot;

@@ -55,6 +55,11 @@ __global__ void zero_kernel(uint4* __restrict__ p, int64_t n16) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// a key that float_key made from a NaN (above +inf's key, or below -inf's)
+__device__ __forceinline__ bool key_is_nan(uint32_t k) {
+  return k > 0xff800000u || k < 0x007fffffu;
+}
+
 __device__ __forceinline__ int row_len(const BatchArgs& b, int t) {
   const int bi = row_request(b.cu, b.B, t);
   return row_visible(b, bi, t);
@@ -82,7 +87,10 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(BatchArgs b,
       kk[u] = float_key(row[min(base + (int)threadIdx.x + u * kHistThreads, s1 - 1)]);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (base + (int)threadIdx.x + u * kHistThreads < s1) atomicAdd(&h[kk[u] >> 21], 1u);
+      if (base + (int)threadIdx.x + u * kHistThreads < s1) {
+        device_check(b, key_is_nan(kk[u]), DSA_CHECK_NAN_SCORE);
+        atomicAdd(&h[kk[u] >> 21], 1u);
+      }
   }
   __syncthreads();
   uint32_t* gh = hist + (int64_t)t * kTopkBins;
@@ -230,6 +238,7 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
     const int s = pos_of(j);
     const int d = (int)(key[j] >> 21);
     if (s < v) {
+      device_check(b, key_is_nan(key[j]), DSA_CHECK_NAN_SCORE);
       if (b1 < 0 || d > b1) am |= (SegMask)1 << j;
       else if (d == b1) em |= (SegMask)1 << j;
     }
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(
   for (int j = 0; j < kPerThread; ++j)
     if ((em >> j) & 1) atomicAdd(&h2[(key[j] >> 10) & (kTopkBins - 1)], 1u);
 
-  // both counts in one scan: at most 8192 per work-group, so 16 bits each
+  // both counts in one scan: at most kCollectSeg (4096) per work-group, so 16 bits each
   uint32_t tot;
   const uint32_t ex = block_exclusive_sum(((uint32_t)__popcll(am) << 16) | (uint32_t)__popcll(em),
                                           wsum, &tot);
@@ -578,7 +587,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     for (int q = 0; q < Q; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (valid(q, e)) atomicAdd(&mine[key[q][e] >> 21], 1u);
+        if (valid(q, e)) {
+          device_check(b, key_is_nan(key[q][e]), DSA_CHECK_NAN_SCORE);
+          atomicAdd(&mine[key[q][e] >> 21], 1u);
+        }
   }
   __syncthreads();
   for (int i = tid; i < kTopkBins; i += kRowThreads) {

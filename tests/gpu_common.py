@@ -2,6 +2,8 @@
 ABI and compare it with the float64 oracle."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -79,40 +81,64 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_scores(gpu_rows: np.ndarray, ref_rows: np.ndarray, vis):
+    worst = 0.0
     for i, v in enumerate(vis):
         g, r = gpu_rows[i, :v], ref_rows[i, :v]
         if v == 0:
             continue
-        tol = SCORE_RTOL * max(np.abs(r).max(), 1e-30)
+        scale = max(np.abs(r).max(), 1e-30)
         err = np.abs(g - r)
-        assert np.all(err <= tol), (i, float(err.max()), tol)
+        worst = max(worst, float(err.max()) / scale)
+        assert np.all(err <= SCORE_RTOL * scale), (i, float(err.max()), SCORE_RTOL * scale)
+    record_margin("score max abs / row max", worst, SCORE_RTOL)
 
 
 def check_selection(gpu_idx: np.ndarray, sel, flags, Ks):
     bad = {}
+    swaps = 0
     for i in range(len(Ks)):
         p = O.selection_check(gpu_idx[i], sel[i], flags[i], Ks[i])
         if p:
             bad[i] = p
+        g = set(int(x) for x in gpu_idx[i] if x >= 0)
+        swaps += len(g - set(sel[i][: int(Ks[i])].tolist()))
+    # positions that differ from the oracle's (all inside the tie band), per row
+    record_margin("selection: tie-band swaps per row", swaps / max(1, len(Ks)), float(K))
     assert not bad, dict(list(bad.items())[:4])
+
+
+# (test, quantity, achieved, bar) of every parity check in the session; the
+# conftest prints them after the run, so the margins show in passing runs too
+MARGINS = []
+
+
+def record_margin(quantity: str, achieved: float, bar: float):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    MARGINS.append((test, quantity, float(achieved), float(bar)))
 
 
 def check_attention(out_gpu: np.ndarray, ref: np.ndarray, lse_gpu=None, lse_ref=None,
                     relative=True):
     err = np.abs(out_gpu - ref)
+    record_margin("attention max abs", err.max(initial=0), OUT_MAX_ABS)
+    record_margin("attention mean abs", err.mean() if err.size else 0.0, OUT_MEAN_ABS)
     assert err.max() <= OUT_MAX_ABS, float(err.max())
     assert err.mean() <= OUT_MEAN_ABS, float(err.mean())
     if relative:
         rms = np.sqrt((ref ** 2).mean(axis=-1, keepdims=True))
         live = rms[..., 0] > 0
         rel = err[live] / rms[live]
+        record_margin("attention max abs / rms", rel.max(initial=0), OUT_MAX_ABS)
+        record_margin("attention mean abs / rms", rel.mean() if rel.size else 0.0, OUT_MEAN_ABS)
         assert rel.max() <= OUT_MAX_ABS, float(rel.max())
         assert rel.mean() <= OUT_MEAN_ABS, float(rel.mean())
     if lse_gpu is not None:
         fin = np.isfinite(lse_ref)
         assert np.array_equal(fin, np.isfinite(lse_gpu))
         assert np.all(np.isneginf(lse_gpu[~fin]))
-        assert np.abs(lse_gpu[fin] - lse_ref[fin]).max(initial=0) <= LSE_ATOL
+        lerr = np.abs(lse_gpu[fin] - lse_ref[fin]).max(initial=0)
+        record_margin("lse max abs", lerr, LSE_ATOL)
+        assert lerr <= LSE_ATOL
     # rows with no selected token are exactly zero
     if lse_ref is not None:
         empty = np.isneginf(lse_ref)

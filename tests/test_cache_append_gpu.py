@@ -122,6 +122,7 @@ def test_cache_append_special_keys():
     _run(cu, L, pt, num_pages, k, kv_new)
 
 
+@pytest.mark.device_check_flags
 def test_cache_append_skips_invalid_pages_and_short_requests():
     rng = np.random.default_rng(9)
     # request 1's last page id lies outside the pool; request 2 is a padding

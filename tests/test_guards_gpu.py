@@ -66,8 +66,12 @@ CASES = [
 
 @pytest.mark.parametrize("ci", range(len(CASES)))
 @pytest.mark.parametrize("mode", ["fused", "mli"])
-def test_decode_step_writes_stay_in_bounds(ci, mode):
+def test_decode_step_writes_stay_in_bounds(ci, mode, request):
     c = CASES[ci]
+    if c["bad"] or mode == "mli":
+        # a page id outside the pool; in MLI mode the previous selection also
+        # names positions past some rows' visible length (skipped)
+        request.applymarker(pytest.mark.device_check_flags)
     b, d = _batch(c["n_q"], c["L"], c["seed"], c["bad"])
     T = d.meta.T
     g = Guarded()
@@ -92,8 +96,10 @@ def test_decode_step_writes_stay_in_bounds(ci, mode):
 
 
 @pytest.mark.parametrize("ci", range(len(CASES)))
-def test_stages_write_in_bounds(ci):
+def test_stages_write_in_bounds(ci, request):
     c = CASES[ci]
+    if c["bad"]:
+        request.applymarker(pytest.mark.device_check_flags)
     b, d = _batch(c["n_q"], c["L"], c["seed"], c["bad"])
     T = d.meta.T
     g = Guarded()

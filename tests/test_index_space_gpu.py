@@ -90,6 +90,7 @@ def test_topk_transform_and_paged_attention_small(ci):
     check_attention(bf16_to_f64(out_p), ref, lse_p.cpu().numpy(), ref_lse)
 
 
+@pytest.mark.device_check_flags
 def test_paged_attention_skips_out_of_range_slots():
     b = synth.make_batch([2, 1], [3000, 5000], seed=71, paging="shuffled", heavy=16,
                          pool_extra_pages=3)
