@@ -255,6 +255,65 @@ def copy_bandwidth(gib=2, iters=10):
     return gbs
 
 
+def read_ceilings(d, iters=20):
+    """HBM read rates this GPU delivers for the scan's bytes: a linear
+    streaming read of the whole key pool, and a load-only pass over the key
+    stream in the scan's own order (each request's pages through its page
+    table, two pages in flight per wave), both from the library's
+    measurement kernels (include/dsa_bench.h)."""
+    import torch
+
+    import sparse_attention_02_amd as dsa
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    k8 = d.k8[0]
+    nbytes = k8.numel()
+    L = d.meta.seqlens_k.cpu().numpy()
+    key_bytes = int(sum((int(x) + 63) // 64 for x in L)) * 64 * 128
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / iters * 1e-3
+
+    t_lin = timed(lambda: dsa.binding.dsa_bench_stream_read(k8, sink))
+    t_key = timed(lambda: dsa.binding.dsa_bench_key_stream_read(d.meta, k8, sink))
+    return {"linear_read_gbs": nbytes / t_lin / 1e9,
+            "key_stream_read_gbs": key_bytes / t_key / 1e9,
+            "key_stream_read_us": t_key * 1e6, "key_stream_bytes": key_bytes}
+
+
+def decode_b32_measure(steps):
+    """The 32-request decode batch (2 rows each, 32768-token contexts): step
+    time, query-tokens/s and the step's algorithmic bytes over its time."""
+    import torch
+
+    import synth
+    from sparse_attention_02_amd import accounting
+    from synth.device import to_device
+    b = synth.make_workload(1)
+    d = to_device(b)
+    step = Step(b, d)
+    ms_step, stage_ms = timed_steps(step, steps, 5)
+    work = accounting.batch_work(b.seqlens_k, b.n_q)
+    res = {"workload": b.name, "query_rows": b.T, "ms_per_step": ms_step,
+           "query_tokens_per_s": b.T / (ms_step * 1e-3),
+           "stages_ms": dict(zip(("index_score", "topk", "attention"), stage_ms)),
+           "algorithmic_bytes": work["bytes"],
+           "achieved_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
+           "frac": work["bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "indexer_gbs": work["indexer_bytes"] / (stage_ms[0] * 1e-3) / 1e9,
+           "attention_gbs": work["attention_bytes"] / (stage_ms[2] * 1e-3) / 1e9}
+    del step, d
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(batch, rows, threads):
     """The float64 oracle over a sample of rows: scores, top-k, attention."""
     import numpy as np
@@ -663,10 +722,16 @@ def main():
         f"{step_gbs:.0f} GB/s")
     space = index_space_measure(b, d) if args.extras else None
     union = union_bytes(b, step.idx) if args.extras else None
+    ceil = read_ceilings(d)
+    log(f"read ceilings: linear {ceil['linear_read_gbs']:.0f} GB/s, key stream in scan order "
+        f"{ceil['key_stream_read_gbs']:.0f} GB/s ({ceil['key_stream_read_us']:.1f} us)")
     del step, d
     torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth()
     log(f"device copy {copy_gbs:.0f} GB/s")
+    b32 = decode_b32_measure(max(20, args.steps // 2))
+    log(f"{b32['workload']}: step {b32['ms_per_step']:.3f} ms, "
+        f"{b32['query_tokens_per_s']:.0f} query-tokens/s, {b32['achieved_gbs']:.0f} GB/s")
 
     result = {
         "metric": METRIC,
@@ -686,7 +751,10 @@ def main():
                    "context": int(b.max_seqlen_k), "topk": synth.TOPK, "page_size": 64,
                    "indexer": "64x128 fp8", "mla": "128 heads x 576 bf16"},
         "step_hbm": {"algorithmic_bytes": work["bytes"], "achieved_gbs": step_gbs,
-                     "frac": step_gbs / HBM_PEAK_GBS, "device_copy_gbs": copy_gbs},
+                     "frac": step_gbs / HBM_PEAK_GBS, "device_copy_gbs": copy_gbs,
+                     "linear_read_gbs": ceil["linear_read_gbs"],
+                     "key_stream_read_gbs": ceil["key_stream_read_gbs"],
+                     "scan_vs_key_stream_read": ceil["key_stream_read_us"] / (ms_idx * 1e3)},
         "stages_ms": {"index_score": ms_idx, "topk": ms_topk, "attention": ms_attn},
         "step_device_ms": step_dev,
         "roofline": {"kernel": "index_score_page_kernel", "bound": "hbm", "achieved": idx_gbs,
@@ -695,6 +763,7 @@ def main():
         "attention_roofline": {"kernel": "sparse_mla_kernel + mla_merge_kernel", "bound": "hbm",
                                "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": attn_gbs / HBM_PEAK_GBS},
+        "decode_b32_mtp1_ctx32768": b32,
     }
     if args.extras:
         result["prefill"] = prefill_measure(max(3, args.steps // 10))

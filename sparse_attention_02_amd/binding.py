@@ -35,7 +35,9 @@ EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_s
            "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
            "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc",
            "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error",
-           "dsa_device_check", "dsa_device_checks_enabled"]
+           "dsa_device_check", "dsa_device_checks_enabled",
+           # measurement kernels (include/dsa_bench.h)
+           "dsa_bench_stream_read", "dsa_bench_key_stream_read"]
 
 
 class DsaError(RuntimeError):
@@ -138,6 +140,10 @@ def _load(path: str) -> ctypes.CDLL:
     L.dsa_device_check.restype = ctypes.c_int
     L.dsa_device_checks_enabled.argtypes = []
     L.dsa_device_checks_enabled.restype = i32
+    L.dsa_bench_stream_read.argtypes = [vp, sz, vp, vp]
+    L.dsa_bench_stream_read.restype = ctypes.c_int
+    L.dsa_bench_key_stream_read.argtypes = [vp, i32, vp, i32, i32, vp, i32, vp, vp]
+    L.dsa_bench_key_stream_read.restype = ctypes.c_int
     _loaded[path] = L
     return L
 
@@ -195,6 +201,21 @@ def dsa_device_check(stream=None) -> int:
     if rc not in (DSA_OK, DSA_ERR_DEVICE_CHECK):
         _check(rc)
     return int(flags.value)
+
+
+def dsa_bench_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement kernel: reads all of src once (include/dsa_bench.h)."""
+    _check(lib().dsa_bench_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                       _stream(stream)))
+
+
+def dsa_bench_key_stream_read(batch: "Batch", k8_cache, sink, stream=None):
+    """Measurement kernel: reads the batch's indexer-key pages the way the
+    scan does and nothing else (include/dsa_bench.h)."""
+    c = batch.c
+    _check(lib().dsa_bench_key_stream_read(_ptr(k8_cache), c.num_pages, c.page_table, c.batch,
+                                           c.max_pages_per_req, c.seqlens_k, c.max_seqlen_k,
+                                           _ptr(sink), _stream(stream)))
 
 
 def dsa_device_checks_enabled() -> bool:

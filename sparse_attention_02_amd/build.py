@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 LIB_CHECKED = os.path.join(PKG, "libdsa_checked.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip",
+           "bench_kernels.hip"]
 # per-file code-generation options: the indexer reads its MFMA results with
 # VALU right away, so they are kept in VGPRs instead of AGPRs
 FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
@@ -36,7 +37,8 @@ def stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(INCLUDE, "dsa.h")]
+    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [
+        os.path.join(INCLUDE, h) for h in ("dsa.h", "dsa_bench.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

@@ -11,12 +11,16 @@ from sparse_attention_02_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", h) for h in os.listdir(os.path.join(ROOT, "include"))
+                 if h.endswith(".h"))
 
 
-def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+def _declared(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +32,7 @@ def L():
 
 
 def test_header_declares_the_four_entry_points():
-    d = _declared()
+    d = _declared([HEADER])
     for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step"):
         assert name in d
 
@@ -46,6 +50,18 @@ def _batch(B_=2, T=4, max_q=2, max_seqlen_k=300, max_pages=5, num_pages=10, ptrs
 
 def _err(L):
     return L.dsa_last_error().decode()
+
+
+def test_bench_kernels_refuse_bad_arguments(L):
+    """The measurement kernels check their host arguments like the path's
+    entry points (nothing launched here)."""
+    sink = 0x1000
+    assert L.dsa_bench_stream_read(0x1008, 64, sink, None) == B.DSA_ERR_INVALID_ARG
+    assert L.dsa_bench_stream_read(0x1000, 63, sink, None) == B.DSA_ERR_INVALID_ARG
+    assert L.dsa_bench_stream_read(0x1000, 0, sink, None) == B.DSA_OK
+    assert L.dsa_bench_key_stream_read(0x1000, 10, 0x2000, 2, 1, 0x3000, 300, sink, None) == \
+        B.DSA_ERR_INVALID_ARG  # 1 page per row cannot hold 300 tokens
+    assert L.dsa_bench_key_stream_read(0x1000, 10, 0x2000, 0, 5, 0x3000, 300, sink, None) == B.DSA_OK
 
 
 def test_status_strings(L):
