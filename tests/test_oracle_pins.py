@@ -585,27 +585,38 @@ def test_sparse_mla_leaves_out_pages_outside_pool():
 # ---------------------------------------------------------------- accounting
 
 def test_accounting_reproduces_printed_table():
+    """The per-pair costs and the decode columns of the printed DSA-versus-
+    dense table of "MTP and sparse attention: NSA and DSA" follow from the
+    library's per-row model (one query row over L cached tokens; dense =
+    attention over every visible token, no indexer).  The prefill columns
+    follow the page's own counting: L*L/2 indexer pairs, L*min(L, k)
+    absorbed-attention pairs, and L*L/2 expanded-attention pairs for dense."""
     with open(os.path.join(GOLDEN, "p1_dsa_accounting.txt")) as f:
         lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
     pair = lines[0]
     assert pair[0] == "pair"
-    assert round(accounting.mla_pair_flops() / 1e3) == int(pair[1])
+    assert round(accounting.attention_pair_flops() / 1e3) == int(pair[1])
     assert round(accounting.indexer_pair_flops() / 1e3) == int(pair[2])
-    assert round(100 * accounting.indexer_bytes_per_token() /
-                 accounting.latent_bytes_per_token()) == int(pair[3])
+    assert round(100 * accounting.indexer_token_bytes() /
+                 accounting.latent_token_bytes()) == int(pair[3])
     for row in lines[1:]:
-        ctx = int(row[0]) * 1024
+        L = int(row[0]) * 1024
         vals = list(map(float, row[1:]))
-        w = accounting.one_query(ctx)
+        sparse = accounting.batch_work([L], [1])  # one query row seeing L tokens
+        dense = accounting.batch_work([L], [1], dense=True)
+        assert sparse["rows"] == dense["rows"] == 1
+        pairs, sel = L * L / 2, min(L, accounting.TOPK)
+        pre_dense = pairs * accounting.expanded_pair_flops()
+        pre_dsa = pairs * accounting.indexer_pair_flops() + L * sel * accounting.attention_pair_flops()
         got = [
-            round(w["decode_flops_dense"] / 1e9, 2), round(w["decode_flops_dsa"] / 1e9, 2),
-            round(w["decode_flops_dense"] / w["decode_flops_dsa"], 1),
-            round(w["decode_bytes_dense"] / 2 ** 20, 1), round(w["decode_bytes_dsa"] / 2 ** 20, 1),
-            round(w["decode_bytes_dense"] / w["decode_bytes_dsa"], 1),
-            round(w["prefill_flops_dense"] / 1e12, 1), round(w["prefill_flops_dsa"] / 1e12, 1),
-            round(w["prefill_flops_dense"] / w["prefill_flops_dsa"], 1),
+            round(dense["flops"] / 1e9, 2), round(sparse["flops"] / 1e9, 2),
+            round(dense["flops"] / sparse["flops"], 1),
+            round(dense["cache_read_bytes"] / 2 ** 20, 1),
+            round(sparse["cache_read_bytes"] / 2 ** 20, 1),
+            round(dense["cache_read_bytes"] / sparse["cache_read_bytes"], 1),
+            round(pre_dense / 1e12, 1), round(pre_dsa / 1e12, 1), round(pre_dense / pre_dsa, 1),
         ]
-        assert got == vals, (ctx, got, vals)
+        assert got == vals, (L, got, vals)
 
 
 def test_batch_work_headline_workload():
@@ -614,3 +625,4 @@ def test_batch_work_headline_workload():
     assert w["indexer_bytes"] == 64 * (131072 * 132 + 4 * 2048) + 128 * (8192 + 4 + 256)
     assert w["indexer_flops"] == sum(16384 * v for v in [131071, 131072] * 64)
     assert w["mla_flops"] == 128 * 2048 * 278528
+    assert w["bytes"] == 1447657984  # the figure the bench divides by
