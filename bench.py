@@ -90,15 +90,31 @@ def _short(name):
     return name.split("(dsa::")[0].split("(float")[0].split("(unsigned")[0][:60]
 
 
+def _grid(r):
+    """The dispatch's grid size (work-items) from a rocprofv3 CSV row."""
+    if r.get("Grid_Size"):
+        return r["Grid_Size"]
+    dims = [r.get(f"Grid_Size_{a}") for a in "XYZ"]
+    return "x".join(d for d in dims if d) or "?"
+
+
 def summarize_trace(d):
+    """Per (kernel, grid size): dispatches of the same kernel on different
+    workloads (the 128K batch and the 32K batch share kernels) stay apart."""
+    import collections
     import csv
     import glob
-    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
-    print("| kernel | calls | avg us | min us | max us | % time |\n|---|---|---|---|---|---|")
+    f = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    agg = collections.defaultdict(list)
     for r in csv.DictReader(open(f)):
-        print(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-              f"{float(r['Percentage']):.2f} |")
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        agg[(_short(r["Kernel_Name"]), _grid(r), r.get("Stream_Id", "?"))].append(ns)
+    total = sum(sum(v) for v in agg.values())
+    print("| kernel | grid (work-items) | stream | calls | avg us | min us | max us | % time |\n"
+          "|---|---|---|---|---|---|---|---|")
+    for (k, g, st), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {k} | {g} | {st} | {len(v)} | {sum(v) / len(v) / 1e3:.1f} | "
+              f"{min(v) / 1e3:.1f} | {max(v) / 1e3:.1f} | {100 * sum(v) / total:.2f} |")
 
 
 def summarize_counters(fetch_dir, write_dir):
@@ -111,16 +127,18 @@ def summarize_counters(fetch_dir, write_dir):
         agg = collections.defaultdict(list)
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == c:
-                agg[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+                agg[(_short(r["Kernel_Name"]), _grid(r), r.get("Queue_Id", "?"))].append(
+                    float(r["Counter_Value"]))
         vals[c] = {k: (len(v), sum(v) / len(v)) for k, v in agg.items()}
-    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |\n"
-          "|---|---|---|---|---|")
+    print("| kernel | grid (work-items) | queue | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | "
+          "HBM bytes (scaled) |\n|---|---|---|---|---|---|---|")
     idx = None
-    for k, (n, fk) in vals["FETCH_SIZE"].items():
-        wk = vals["WRITE_SIZE"].get(k, (0, 0.0))[1]
+    for (k, g, qu), (n, fk) in vals["FETCH_SIZE"].items():
+        wk = vals["WRITE_SIZE"].get((k, g, qu), (0, 0.0))[1]
         hbm = 1024 * (FETCH_SCALE * fk + WRITE_SCALE * wk)
-        print(f"| {k} | {n} | {fk:.0f} | {wk:.0f} | {hbm:.4g} |")
-        if k.startswith("index_score"):
+        print(f"| {k} | {g} | {qu} | {n} | {fk:.0f} | {wk:.0f} | {hbm:.4g} |")
+        # the 128K batch's scan: the largest launch of the page kernel
+        if k.startswith("index_score_page") and (idx is None or hbm > idx):
             idx = hbm
     print(f"\nfetch_scale: {FETCH_SCALE}\nwrite_scale: {WRITE_SCALE}")
     if idx is not None:
@@ -298,8 +316,11 @@ def decode_b32_measure(steps):
     from synth.device import to_device
     b = synth.make_workload(1)
     d = to_device(b)
-    step = Step(b, d)
-    ms_step, stage_ms = timed_steps(step, steps, 5)
+    # on a stream of its own (default priority), so that kernel traces keep
+    # its launches apart from the 128K batch's launches of the same kernels
+    with torch.cuda.stream(torch.cuda.Stream()):
+        step = Step(b, d)
+        ms_step, stage_ms = timed_steps(step, steps, 5)
     work = accounting.batch_work(b.seqlens_k, b.n_q)
     res = {"workload": b.name, "query_rows": b.T, "ms_per_step": ms_step,
            "query_tokens_per_s": b.T / (ms_step * 1e-3),
@@ -419,17 +440,19 @@ def summarize_mfma(d, simds=1024):
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     n_xcd = 8
     for r in csv.DictReader(open(f)):
-        agg[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    print("| kernel | dispatches | MFMA busy cycles (sum over SIMDs) | active cycles per XCD | "
-          "MFMA busy % |\n|---|---|---|---|---|")
-    for k, v in agg.items():
+        agg[(_short(r["Kernel_Name"]), _grid(r), r.get("Queue_Id", "?"))][
+            r["Counter_Name"]].append(float(r["Counter_Value"]))
+    print("| kernel | grid (work-items) | queue | dispatches | MFMA busy cycles (sum over SIMDs) "
+          "| active cycles per XCD | MFMA busy % |\n|---|---|---|---|---|---|---|")
+    for (k, g, qu), v in agg.items():
         busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES")
         act = v.get("GRBM_GUI_ACTIVE")
         if not busy or not act or sum(busy) == 0:
             continue
         b_avg = sum(busy) / len(busy)
         a_avg = sum(act) / len(act) / n_xcd
-        print(f"| {k} | {len(busy)} | {b_avg:.4g} | {a_avg:.4g} | {100 * b_avg / (a_avg * simds):.1f} |")
+        print(f"| {k} | {g} | {qu} | {len(busy)} | {b_avg:.4g} | {a_avg:.4g} | "
+              f"{100 * b_avg / (a_avg * simds):.1f} |")
 
 
 # bytes one appended token moves: its bf16 key (256) and latent row (1152)
