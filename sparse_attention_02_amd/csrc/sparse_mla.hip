@@ -12,9 +12,10 @@
 // heads, so each gathered latent row is read from HBM once per row.  Per
 // tile of 32 selected tokens:
 //   gather   slots come from a per-split table built once (position -> page
-//            -> slot); the 1152-byte rows go straight from HBM into LDS with
-//            global_load_lds_dwordx4 (row pitch 1184 bytes) into a ring of
-//            three buffers;
+//            -> slot); each 1152-byte row goes straight from HBM into LDS
+//            (global_load_lds, a 1024-byte and a 128-byte piece at a
+//            wave-uniform address; row pitch 1184 bytes) into a ring of three
+//            buffers;
 //   S^T      = KV Q^T, wave w taking heads 16w .. 16w+15 (v_mfma_f32_16x16x32_bf16;
 //            the latent part of its query is held in registers, the rope
 //            part in LDS);
@@ -36,6 +37,8 @@
 // and the scores of tile i+1 while tile i+2 streams in, with one barrier per
 // step.  Operand reads run ahead of the products that use them (two k-steps
 // in S^T, one head block in O^T), fixed with scheduling fences.
+#include <cfloat>
+
 #include "device_common.h"
 
 namespace dsa {
@@ -47,9 +50,7 @@ constexpr int kThreads = 512;
 // conflict-free when the pitch is 32 mod 64 bytes (measured: 1152 or 1168
 // bytes cost 1.65-3x more).
 constexpr int kKsPitch = 1184;                 // bytes per token row of the gathered tile
-constexpr int kKsChunks = kKsPitch / 16;       // 74 (72 data + 2 pad)
-constexpr int kKsLoads = (kMlaTile * kKsChunks + 63) / 64;  // 37 wave-wide 1 KB loads
-constexpr int kKsBytes = kKsLoads * 1024;      // 37888
+constexpr int kKsBytes = kMlaTile * kKsPitch;  // 37888
 constexpr int kMaxChunk = 2048;                // selected tokens per split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -232,34 +233,29 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   // bit x: token x of the tile has a row
   auto tile_bits = [&](int sv) -> uint32_t { return (uint32_t)__ballot(sv >= 0); };
 
-  // one tile: 37 wave-wide loads of 64 x 16 bytes; lane L of load n fills
-  // byte 16*(64n + L) of the buffer = token (64n+L)/74, chunk (64n+L)%74.
-  // The 64 lanes of a load span at most two tokens, whose slots come from
-  // the tile's slot vector by lane reads (no LDS round trip per load).
+  // one tile, one token row at a time: wave w fetches rows 4w .. 4w+3, each
+  // with a 1024-byte load (16 bytes a lane) and a 128-byte one (4 bytes on
+  // each of 32 lanes; LDS-bound loads narrower than a dword still fill a
+  // dword per lane) into the row's place in the tile.  A row's slot is the
+  // same for the whole wave, so its address is a scalar base plus a fixed
+  // lane offset (no per-lane address arithmetic); a skipped row re-reads a
+  // valid one, so every row the products touch holds finite cache data.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t tail_ofs = 1024u + 4u * (uint32_t)lane;  // bytes 1024 .. 1151 of a row (lanes < 32)
   auto issue_gather = [&](int sv, uint32_t bits, unsigned char* dst) {
     if (bits == 0) return;
     const int fb = __builtin_amdgcn_readlane(sv, __builtin_ctz(bits));
-    // recomputed on every call: keeping the per-load offsets live across
-    // the tile loop would cost registers
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int i = 0; i < (kKsLoads + 7) / 8; ++i) {
-      const int n = wave_u + 8 * i;
-      if (n < kKsLoads) {
-        const int ta = (64 * n) / kKsChunks;  // first token of the load
-        const int sa = __builtin_amdgcn_readlane(sv, ta);
-        const int sb = __builtin_amdgcn_readlane(sv, min(ta + 1, kMlaTile - 1));
-        const int c = 64 * n + ln;
-        const int tok = c / kKsChunks;
-        int cc = c - tok * kKsChunks;
-        int slot = tok == ta ? sa : sb;
-        if (slot < 0) slot = fb;  // skipped tokens re-read a valid row
-        if (cc >= 72) cc = 0;     // pad chunks
-        const uint16_t* src = kv + (int64_t)slot * DSA_MLA_DIM + cc * 8;
-        __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
-      }
+    for (int i = 0; i < kMlaTile / 8; ++i) {
+      const int r = 4 * wave_u + i;
+      int slot = __builtin_amdgcn_readlane(sv, r);
+      if (slot < 0) slot = fb;
+      const uint16_t* row = kv + (int64_t)slot * DSA_MLA_DIM;
+      unsigned char* d = dst + r * kKsPitch;
+      __builtin_amdgcn_global_load_lds(row + 8 * lane, d, 16, 0, 0);
+      if (lane < 32)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const unsigned char*>(row) + tail_ofs, d + 1024, 4, 0, 0);
     }
   };
 
@@ -269,7 +265,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int hb = 0; hb < 8; ++hb) acc[db][hb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference max of this lane's head (log2 units)
+  float m_ref = -FLT_MAX;  // reference max of this lane's head (log2 units)
   float l_run = 0.f;
   const int d_base = kDimsPerWave * wave;
 
@@ -303,10 +299,18 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     }
     // lane holds tokens 4g + r (s0) and 16 + 4g + r (s1) of head `head`
     float z[8];
+    if (mask == ~0u) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      z[r] = (mask >> (4 * g + r)) & 1u ? s0[r] * scale_log2 : -INFINITY;
-      z[4 + r] = (mask >> (16 + 4 * g + r)) & 1u ? s1[r] * scale_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        z[r] = s0[r] * scale_log2;
+        z[4 + r] = s1[r] * scale_log2;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[r] = (mask >> (4 * g + r)) & 1u ? s0[r] * scale_log2 : -INFINITY;
+        z[4 + r] = (mask >> (16 + 4 * g + r)) & 1u ? s1[r] * scale_log2 : -INFINITY;
+      }
     }
     float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
                        fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
@@ -318,22 +322,20 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
                                                      false, false);
       tmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
     }
-    // while the reference is -inf nothing has been accumulated, so the
-    // first finite maximum needs no rescale (alpha stays 1)
-    const bool raise = tmax > m_ref + kRescaleMargin || (m_ref == -INFINITY && tmax > -INFINITY);
+    // the reference starts at -FLT_MAX, below every finite score, so the
+    // first finite maximum always raises it (with a factor of 0 for the
+    // empty accumulator) and z - m_ref is never inf - inf
+    const bool raise = tmax > m_ref + kRescaleMargin;
     const float m_new = raise ? tmax : m_ref;
-    const float alpha = m_ref == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
     l_run *= alpha;
     m_ref = m_new;
     st.alpha[head] = alpha;  // the four lanes of a head store the same value
     st.raised[wave] = __ballot(alpha != 1.f) != 0;
     float p[8];
-    float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p[r] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-      psum += p[r];
-    }
+    for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
+    const float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     l_run += psum;
     st.P[wave * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
