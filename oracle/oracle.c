@@ -391,6 +391,113 @@ void oracle_dense_mla(const oracle_batch* bt, int64_t num_pages, int32_t H, int3
   run_items((int64_t)n_rows * H, threads, mla_item, &c);
 }
 
+/* ---- expanded multi-head attention (masked MHA) ---------------------------
+ * "MTP and sparse attention: NSA and DSA", caveat on short-sequence prefill
+ * and the per-pair accounting beside the DSA table: dense prefill runs the
+ * expanded multi-head form, 2*H*(128 + 64) + 2*H*128 FLOPs per pair (scores
+ * over 128 up-projected key dims plus the 64 shared rope dims, values of 128
+ * up-projected dims per head), and the V3.2 report emulates DSA's selection
+ * in that form with a mask ("masked MHA mode").  Per row t and head h, over
+ * the positions S_t the row attends (idx[t] when given, else every visible
+ * position; positions on a page outside the pool are left out):
+ *   kn(s,d) = sum_c w_uk(h,d,c) c(s,c),   vn(s,d) = sum_c w_uv(h,d,c) c(s,c)
+ *   z(s) = sm_scale * (sum_d qn(t,h,d) kn(s,d) + sum_r qr(t,h,r) kv(s,512+r))
+ *   o(t,h,d) = sum_s softmax(z)(s) vn(s,d),  lse = m + ln sum_s exp(z(s) - m)
+ * with c(s,.) the first 512 dims of the cached latent row, d < 128, r < 64.
+ * Layouts: qn [T][H][128], qr [T][H][64], w_uk and w_uv [H][128][512], all
+ * bf16; kv [pages*64][576] bf16.
+ */
+typedef struct {
+  const oracle_batch* bt;
+  int32_t H;
+  const uint16_t *qn, *qr, *w_uk, *w_uv, *kv;
+  const int32_t* idx;
+  int32_t k;
+  double sm_scale;
+  const int32_t* rows;
+  double* out;
+  double* lse;
+  int64_t num_pages;
+} mha_ctx;
+
+enum { MHA_DN = 128, MHA_DR = 64, MHA_C = 512, MHA_KV = 576 };
+
+static void mha_item(void* p, int64_t item) {
+  mha_ctx* c = (mha_ctx*)p;
+  int64_t i = item / c->H;
+  int32_t h = (int32_t)(item % c->H);
+  int32_t t = c->rows[i];
+  int32_t b = oracle_row_request(c->bt, t);
+  int64_t v = b < 0 ? 0 : oracle_row_visible(c->bt, t);
+  double* o = c->out + (i * c->H + h) * MHA_DN;
+  for (int d = 0; d < MHA_DN; ++d) o[d] = 0.0;
+  int64_t n = 0;
+  int64_t cap = c->idx ? c->k : v;
+  int64_t* S = (int64_t*)malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
+  if (c->idx) {
+    for (int32_t j = 0; j < c->k; ++j) {
+      int32_t s = c->idx[i * c->k + j];
+      if (s >= 0 && s < v && oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
+    }
+  } else {
+    for (int64_t s = 0; s < v; ++s)
+      if (oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
+  }
+  if (n == 0) {
+    c->lse[i * c->H + h] = -INFINITY;
+    free(S);
+    return;
+  }
+  double qn[MHA_DN], qr[MHA_DR];
+  for (int d = 0; d < MHA_DN; ++d)
+    qn[d] = oracle_bf16_decode(c->qn[((int64_t)t * c->H + h) * MHA_DN + d]);
+  for (int r = 0; r < MHA_DR; ++r)
+    qr[r] = oracle_bf16_decode(c->qr[((int64_t)t * c->H + h) * MHA_DR + r]);
+  const uint16_t* wk = c->w_uk + (int64_t)h * MHA_DN * MHA_C;
+  const uint16_t* wv = c->w_uv + (int64_t)h * MHA_DN * MHA_C;
+  double* z = (double*)malloc(sizeof(double) * (size_t)n);
+  double* vn = (double*)malloc(sizeof(double) * (size_t)n * MHA_DN);
+  double lat[MHA_C];
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    const uint16_t* row = c->kv + oracle_slot(c->bt, b, S[j]) * MHA_KV;
+    for (int x = 0; x < MHA_C; ++x) lat[x] = oracle_bf16_decode(row[x]);
+    double dot = 0.0;
+    for (int d = 0; d < MHA_DN; ++d) {
+      double kn = 0.0, vv = 0.0;
+      for (int x = 0; x < MHA_C; ++x) {
+        kn += oracle_bf16_decode(wk[d * MHA_C + x]) * lat[x];
+        vv += oracle_bf16_decode(wv[d * MHA_C + x]) * lat[x];
+      }
+      dot += qn[d] * kn;
+      vn[j * MHA_DN + d] = vv;
+    }
+    for (int r = 0; r < MHA_DR; ++r) dot += qr[r] * oracle_bf16_decode(row[MHA_C + r]);
+    z[j] = c->sm_scale * dot;
+    if (z[j] > m) m = z[j];
+  }
+  double sum = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    z[j] = exp(z[j] - m);
+    sum += z[j];
+  }
+  for (int64_t j = 0; j < n; ++j)
+    for (int d = 0; d < MHA_DN; ++d) o[d] += z[j] / sum * vn[j * MHA_DN + d];
+  c->lse[i * c->H + h] = m + log(sum);
+  free(vn);
+  free(z);
+  free(S);
+}
+
+void oracle_masked_mha(const oracle_batch* bt, int64_t num_pages, int32_t H, const uint16_t* qn,
+                       const uint16_t* qr, const uint16_t* w_uk, const uint16_t* w_uv,
+                       const uint16_t* kv, const int32_t* idx, int32_t k, double sm_scale,
+                       const int32_t* rows, int32_t n_rows, double* out, double* lse,
+                       int threads) {
+  mha_ctx c = {bt, H, qn, qr, w_uk, w_uv, kv, idx, k, sm_scale, rows, out, lse, num_pages};
+  run_items((int64_t)n_rows * H, threads, mha_item, &c);
+}
+
 /* ---- cache append ---------------------------------------------------------
  * "MTP and sparse attention: NSA and DSA", new demands on inference engines:
  * the indexer keys are a second paged cache beside the latent, stored as

@@ -56,6 +56,8 @@ def lib():
         L.oracle_row_visible.argtypes = [bp, i32]
         L.oracle_row_visible.restype = i64
         L.oracle_index_score.argtypes = [bp, i64, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, ci]
+        L.oracle_masked_mha.argtypes = [bp, i64, i32, vp, vp, vp, vp, vp, vp, i32, dbl, vp, i32,
+                                        vp, vp, ci]
         L.oracle_topk.argtypes = [vp, i64, i32, dbl, vp, vp, vp]
         L.oracle_topk.restype = i32
         L.oracle_topk_rows.argtypes = [vp, i64, vp, i32, i32, dbl, vp, vp, i64, vp, vp, ci]
@@ -185,6 +187,30 @@ def dense_mla(meta: Meta, q, kv, rows, sm_scale, dv=512, threads=0):
     lse = np.empty((len(rows), H), np.float64)
     lib().oracle_dense_mla(meta.ref(), kv.shape[0], H, D, dv, _p(q), _p(kv), float(sm_scale),
                            _p(rows), len(rows), _p(out), _p(lse), threads)
+    return out, lse
+
+
+def masked_mha(meta: Meta, q_nope, q_rope, w_uk, w_uv, kv, idx, rows, sm_scale, threads=0):
+    """float64 (out [n, H, 128], lse [n, H]) of the expanded multi-head form
+    over the positions idx[i] (-1 = none), or every visible position when idx
+    is None; positions on a page id outside the pool are left out."""
+    qn = np.ascontiguousarray(q_nope, np.uint16)
+    qr = np.ascontiguousarray(q_rope, np.uint16)
+    wk = np.ascontiguousarray(w_uk, np.uint16)
+    wv = np.ascontiguousarray(w_uv, np.uint16)
+    kv = np.ascontiguousarray(kv, np.uint16)
+    H = qn.shape[1]
+    rows = np.ascontiguousarray(rows, np.int32)
+    k = 0
+    ip = None
+    if idx is not None:
+        idx = np.ascontiguousarray(idx, np.int32)
+        k = idx.shape[1]
+        ip = _p(idx)
+    out = np.empty((len(rows), H, 128), np.float64)
+    lse = np.empty((len(rows), H), np.float64)
+    lib().oracle_masked_mha(meta.ref(), kv.shape[0], H, _p(qn), _p(qr), _p(wk), _p(wv), _p(kv),
+                            ip, k, float(sm_scale), _p(rows), len(rows), _p(out), _p(lse), threads)
     return out, lse
 
 

@@ -626,3 +626,118 @@ def test_batch_work_headline_workload():
     assert w["indexer_flops"] == sum(16384 * v for v in [131071, 131072] * 64)
     assert w["mla_flops"] == 128 * 2048 * 278528
     assert w["bytes"] == 1447657984  # the figure the bench divides by
+
+
+# ------------------------------------------- masked MHA (expanded multi-head form)
+
+def _mha_inputs(rng, T, H=128, integral=False):
+    """q_nope, q_rope, w_uk, w_uv as bf16 bits.  integral: q_nope and w_uk in
+    {-1, 0, 1}, so that w_uk^T q_nope is an integer of magnitude <= 128,
+    exact in bf16."""
+    if integral:
+        qn = rng.integers(-1, 2, size=(T, H, 128)).astype(np.float32)
+        wk = rng.integers(-1, 2, size=(H, 128, 512)).astype(np.float32)
+    else:
+        qn = rng.standard_normal((T, H, 128)).astype(np.float32)
+        wk = (rng.standard_normal((H, 128, 512)) / math.sqrt(512)).astype(np.float32)
+    qr = rng.standard_normal((T, H, 64)).astype(np.float32)
+    wv = (rng.standard_normal((H, 128, 512)) / math.sqrt(512)).astype(np.float32)
+    return _bf16_bits(qn), _bf16_bits(qr), _bf16_bits(wk), _bf16_bits(wv)
+
+
+@pytest.mark.parametrize("with_idx", [False, True])
+def test_masked_mha_is_the_up_projected_absorbed_attention(with_idx):
+    """The expanded form against the absorbed one (the oracle's latent
+    attention, pinned above): with q_latent(h) = W_UK(h)^T q_nope(h) both
+    give the same scores, so the expanded output is W_UV(h) times the
+    absorbed 512-dim output and the lse is the same -- a transposed weight,
+    a dropped rope term or a wrong head fails it."""
+    rng = np.random.default_rng(30)
+    b = _mla_case(rng, 300, n_q=2, scale=0.05)
+    meta = O.Meta.of(b)
+    qn, qr, wk, wv = _mha_inputs(rng, 2, integral=True)
+    q_lat = np.einsum("hdc,thd->thc", _bf16(wk), _bf16(qn))
+    assert np.all(q_lat == np.round(q_lat)) and np.abs(q_lat).max() <= 128
+    q_abs = np.concatenate([_bf16_bits(q_lat), qr], axis=-1)
+    assert np.array_equal(_bf16(q_abs[..., :512]), q_lat)
+    idx = None
+    if with_idx:
+        idx = np.full((2, 96), -1, np.int32)
+        idx[0, :80] = rng.choice(299, 80, replace=False)
+        idx[1, :90] = rng.choice(300, 90, replace=False)
+        lo, ll = O.sparse_mla(meta, q_abs, b.kv[0], idx, [0, 1], synth.SM_SCALE)
+    else:
+        lo, ll = O.dense_mla(meta, q_abs, b.kv[0], [0, 1], synth.SM_SCALE)
+    eo, el = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], idx, [0, 1], synth.SM_SCALE)
+    ref = np.einsum("hdc,thc->thd", _bf16(wv), lo)
+    assert np.allclose(eo, ref, rtol=1e-9, atol=1e-12)
+    assert np.allclose(el, ll, rtol=1e-12, atol=1e-12)
+
+
+def test_masked_mha_matches_torch_attention():
+    """Random (non-integral) weights: the expanded keys and values by torch
+    float64 matmuls, then torch's softmax and logsumexp."""
+    rng = np.random.default_rng(31)
+    b = _mla_case(rng, 140, n_q=1, scale=0.5)
+    meta = O.Meta.of(b)
+    qn, qr, wk, wv = _mha_inputs(rng, 1)
+    eo, el = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], None, [0], synth.SM_SCALE)
+    keys = torch.from_numpy(_logical_rows(b))              # [140, 576]
+    kn = torch.einsum("hdc,sc->hsd", torch.from_numpy(_bf16(wk)), keys[:, :512])
+    vn = torch.einsum("hdc,sc->hsd", torch.from_numpy(_bf16(wv)), keys[:, :512])
+    z = (torch.einsum("hd,hsd->hs", torch.from_numpy(_bf16(qn[0])), kn) +
+         torch.from_numpy(_bf16(qr[0])) @ keys[:, 512:].T) * synth.SM_SCALE
+    o = torch.einsum("hs,hsd->hd", torch.softmax(z, dim=-1), vn)
+    assert np.allclose(eo[0], o.numpy(), rtol=1e-10, atol=1e-13)
+    assert np.allclose(el[0], torch.logsumexp(z, dim=-1).numpy(), rtol=1e-12)
+
+
+def test_masked_mha_special_cases():
+    rng = np.random.default_rng(32)
+    b = _mla_case(rng, 200, scale=0.5)
+    meta = O.Meta.of(b)
+    qn, qr, wk, wv = _mha_inputs(rng, 1)
+    keys = _logical_rows(b)
+    W = _bf16(wv)
+    # one selected position: its up-projected value row, for every head
+    idx = np.full((1, 16), -1, np.int32)
+    idx[0, 5] = 77
+    o, l = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], idx, [0], synth.SM_SCALE)
+    assert np.allclose(o[0], W @ keys[77, :512], rtol=1e-12, atol=1e-14)
+    # zero queries: uniform weights, the mean of the value rows, lse = ln n
+    sel = np.array([[5, 9, 150, 33, -1, 199, 250]], np.int32)  # 250 is past the row
+    z = np.zeros_like(qn), np.zeros_like(qr)
+    o, l = O.masked_mha(meta, z[0], z[1], wk, wv, b.kv[0], sel, [0], synth.SM_SCALE)
+    mean = W @ keys[[5, 9, 150, 33, 199], :512].mean(axis=0)
+    assert np.allclose(o[0], mean, rtol=1e-12, atol=1e-14)
+    assert np.allclose(l[0], math.log(5), rtol=1e-14)
+    # a position the row does not attend leaves the result alone
+    kv = b.kv[0].copy().reshape(-1, 576)
+    kv[int(b.page_table[0, 100 // 64]) * 64 + 100 % 64] = kv[0]
+    o1, l1 = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], sel[:, :4], [0], synth.SM_SCALE)
+    o2, l2 = O.masked_mha(meta, qn, qr, wk, wv, kv.reshape(b.kv[0].shape), sel[:, :4], [0],
+                          synth.SM_SCALE)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # every visible position listed equals no list (plain causal)
+    full = np.arange(200, dtype=np.int32)[None, :]
+    o1, l1 = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], full, [0], synth.SM_SCALE)
+    o2, l2 = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], None, [0], synth.SM_SCALE)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # nothing attended: zeros and -inf
+    o, l = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], np.full((1, 4), -1, np.int32), [0],
+                        synth.SM_SCALE)
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_masked_mha_page_permutation_invariant():
+    rng = np.random.default_rng(33)
+    b = _mla_case(rng, 330, scale=0.5)
+    meta = O.Meta.of(b)
+    qn, qr, wk, wv = _mha_inputs(rng, 1)
+    o1, l1 = O.masked_mha(meta, qn, qr, wk, wv, b.kv[0], None, [0], synth.SM_SCALE)
+    perm = rng.permutation(b.num_pages).astype(np.int32)
+    kv2 = np.empty_like(b.kv[0])
+    kv2[perm] = b.kv[0]
+    o2, l2 = O.masked_mha(O.Meta(b.cu_seqlens_q, b.seqlens_k, perm[b.page_table]), qn, qr, wk,
+                          wv, kv2, None, [0], synth.SM_SCALE)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
