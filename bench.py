@@ -589,15 +589,21 @@ def short_measure(steps):
 def short_prefill_measure(steps, n=4096):
     """A prefill chunk on an empty cache (n rows, row j sees j + 1 tokens):
     the sparse step (indexer over the causal n x n block, top-2048, sparse
-    attention) against dense causal attention over every visible token
-    (dsa_dense_mla_decode), the trade-off the pages quote for short
-    prefills.  Different computations beyond 2048 visible tokens: this only
-    times them."""
+    attention in the absorbed form) against the masked multi-head form the
+    pages give for short prefills (the same indexer and top-k, then the
+    expanded attention over the selection: up-projection of the latent
+    rows, selection mask, flash attention), and against dense absorbed
+    attention over every visible token (dsa_dense_mla_decode).  The sparse
+    step and the masked form compute the same attention (up to the W_UV
+    projection the absorbed output still needs); the dense absorbed one
+    attends more positions beyond 2048 and is only timed."""
+    import numpy as np
     import torch
 
     import sparse_attention_02_amd as dsa
     import synth
     from synth.device import to_device
+    from sparse_attention_02_amd import accounting
     b = synth.make_batch([n], [n], seed=84, paging="identity", heavy=64, pool_extra_pages=1)
     d = to_device(b)
     step = Step(b, d)
@@ -608,14 +614,51 @@ def short_prefill_measure(steps, n=4096):
         dsa.dsa_dense_mla_decode(d.meta, d.q[0], d.kv[0], synth.SM_SCALE, step.out, step.lse, 0,
                                  ws, mk)
 
-    sparse_ms, dense_ms = [], []
+    # the masked multi-head step: indexer, top-k, expanded attention
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda()
+    qn, qr, wk, wv = (dev(a) for a in synth.mha_inputs(85, b.T))
+    ld = (n + 63) // 64 * 64
+    scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
+    tk = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, d.meta, synth.TOPK)
+    ws_t = torch.empty(max(tk, 1), dtype=torch.uint8, device="cuda")
+    mm = dsa.dsa_workspace_size(dsa.DSA_OP_MASKED_MHA, d.meta, 1, 0)
+    ws_m = torch.empty(mm, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((b.T, synth.TOPK), dtype=torch.int32, device="cuda")
+    out_m = torch.empty((b.T, 128, 128), dtype=torch.bfloat16, device="cuda")
+    lse_m = torch.empty((b.T, 128), dtype=torch.float32, device="cuda")
+
+    def select():
+        dsa.dsa_index_score(d.meta, d.q8, d.q_scale, d.w, d.k8[0], d.k_scale[0], scores, ld)
+        dsa.dsa_topk(d.meta, scores, ld, synth.TOPK, idx, ws_t, tk)
+
+    def masked_attention():
+        dsa.dsa_masked_mha_prefill(d.meta, qn, qr, wk, wv, d.kv[0], idx, synth.TOPK,
+                                   synth.SM_SCALE, out_m, lse_m, ws_m, mm)
+
+    def masked_step():
+        select()
+        masked_attention()
+
+    select()
+    sparse_ms, dense_ms, mstep_ms, mattn_ms = [], [], [], []
     for _ in range(3):
         sparse_ms.append(wall_ms(step, steps))
         dense_ms.append(wall_ms(dense, steps))
+        mstep_ms.append(wall_ms(masked_step, steps))
+        mattn_ms.append(wall_ms(masked_attention, steps))
     res = {"workload": f"prefill-{n}-on-empty-cache", "query_rows": b.T,
-           "ms_sparse_step": min(sparse_ms), "ms_dense_attention": min(dense_ms)}
+           "ms_sparse_step": min(sparse_ms), "ms_dense_attention": min(dense_ms),
+           "ms_masked_mha_step": min(mstep_ms), "ms_masked_mha_attention": min(mattn_ms)}
     res["sparse_over_dense"] = res["ms_sparse_step"] / res["ms_dense_attention"]
-    del step, d, ws
+    res["sparse_over_masked_mha_step"] = res["ms_sparse_step"] / res["ms_masked_mha_step"]
+    # the masked form's work: every causal pair at the expanded per-pair
+    # cost, plus the up-projection of the n cached rows (2 x 128 heads x 128
+    # dims x 512 per row, keys and values)
+    pairs = n * (n + 1) // 2
+    flops = pairs * accounting.expanded_pair_flops() + n * 2 * 2 * 128 * 128 * 512
+    res["masked_mha_attention_tflops"] = flops / (res["ms_masked_mha_attention"] * 1e-3) / 1e12
+    res["masked_mha_attention_frac_bf16_peak"] = res["masked_mha_attention_tflops"] / 2500.0
+    del step, d, ws, scores, ws_t, ws_m
     torch.cuda.empty_cache()
     return res
 

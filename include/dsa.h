@@ -220,6 +220,44 @@ int dsa_dense_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint
                          float sm_scale, uint16_t* out, float* lse, int32_t n_split, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* Masked multi-head attention in the expanded form, for short prefills
+ * ("MTP and sparse attention: NSA and DSA", the caveat on short-sequence
+ * prefill and the per-pair accounting beside the DSA table: dense prefill
+ * attends in the expanded multi-head form at 2*H*(128+64) + 2*H*128 FLOPs
+ * per pair, a third of the absorbed form's, and the DeepSeek-V3.2 report
+ * emulates DSA's selection in it with a mask).  Per row t and head h, over
+ * the positions the row attends -- those idx[t] lists (entries < 0 or >= v_t
+ * are ignored), or every visible position 0 .. v_t-1 when idx is NULL --
+ * leaving out positions on a page id outside the pool:
+ *   z(s)     = sm_scale * (q_nope[t,h] . (W_UK[h] c(s)) + q_rope[t,h] . r(s))
+ *   out[t,h] = sum_s softmax(z)(s) * (W_UV[h] c(s))
+ *   lse[t,h] = ln sum_s e^z(s)
+ * with c(s) the first 512 and r(s) the last 64 dims of position s's cached
+ * row.  The library first writes W_UK[h] c(s) and W_UV[h] c(s) of every
+ * cached position of each request into the workspace (bf16), then attends
+ * over them in 64-position tiles.
+ *  q_nope   bf16 [T, 128, 128]  query dims that meet the up-projected keys
+ *  q_rope   bf16 [T, 128, 64]   query dims that meet the rope dims
+ *  w_uk     bf16 [128, 128, 512] head h's key up-projection (row d: key dim d)
+ *  w_uv     bf16 [128, 128, 512] head h's value up-projection
+ *  kv_cache bf16 [num_pages, 64, 576] latent cache by physical slot
+ *  idx      int32 [T, k] logical positions (distinct within a row), or NULL
+ *  k        entries per idx row (1 .. 8192; ignored when idx is NULL)
+ *  sm_scale softmax scale on the 192-dim dot product (1/sqrt(192) for DSA)
+ *  out      bf16 [T, 128, 128] out: rounded to nearest even; zeros for a row
+ *           that attends nothing
+ *  lse      f32 [T, 128] out (may be NULL); -inf for a row that attends nothing
+ *  ws       >= dsa_workspace_size(DSA_OP_MASKED_MHA, batch, k, 0) bytes:
+ *           B * 128 * lp * 512 + B * lp * 128 + T * lp / 8 bytes, lp =
+ *           max_seqlen_k rounded up to 64
+ * Every pointer 16-byte aligned.
+ * Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED (max_seqlen_k > 65536). */
+int dsa_masked_mha_prefill(const dsa_batch_t* batch, const uint16_t* q_nope,
+                           const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv,
+                           const uint16_t* kv_cache, const int32_t* idx, int32_t k,
+                           float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* Indexer inputs of one layer (device pointers, layouts as dsa_index_score). */
 typedef struct {
   const uint8_t* q8;
@@ -354,7 +392,8 @@ typedef enum {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA = 2,
   DSA_OP_DECODE_STEP = 3,
-  DSA_OP_DENSE_MLA = 4 /* k is not used */
+  DSA_OP_DENSE_MLA = 4, /* k is not used */
+  DSA_OP_MASKED_MHA = 5 /* k and n_split are not used */
 } dsa_op;
 
 /* Workspace bytes an op needs for this batch, k and n_split (0 = the

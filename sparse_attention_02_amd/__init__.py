@@ -10,4 +10,5 @@ from .binding import (  # noqa: F401
     dsa_dense_mla_decode, dsa_default_splits, dsa_index_score, dsa_sparse_mla_decode,
     dsa_sparse_mla_decode_paged, dsa_topk, dsa_topk_transform, dsa_workspace_size, lib,
     dsa_device_check, dsa_device_checks_enabled, DSA_CHECK_INDEX, DSA_CHECK_METADATA,
-    DSA_CHECK_NAN_SCORE, DSA_CHECK_PAGE_ID, DSA_ERR_DEVICE_CHECK, checked)
+    DSA_CHECK_NAN_SCORE, DSA_CHECK_PAGE_ID, DSA_ERR_DEVICE_CHECK, checked,
+    DSA_OP_MASKED_MHA, dsa_masked_mha_prefill)

@@ -26,6 +26,7 @@ if os.environ.get("DSA_DEVICE_CHECKS", "0") not in ("", "0"):
  DSA_ERR_DEVICE_CHECK) = range(6)
 DSA_CHECK_PAGE_ID, DSA_CHECK_INDEX, DSA_CHECK_NAN_SCORE, DSA_CHECK_METADATA = 1, 2, 4, 8
 DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP, DSA_OP_DENSE_MLA = 1, 2, 3, 4
+DSA_OP_MASKED_MHA = 5
 DSA_MODE_FUSED, DSA_MODE_MLI = 0, 1
 DSA_STAGE_INDEX_SCORE, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_NUM_STAGES = 0, 1, 2, 3
 DSA_IDX_LOGICAL, DSA_IDX_PAGED, DSA_IDX_RAGGED = 0, 1, 2
@@ -34,6 +35,7 @@ PAGE_SIZE, IDX_HEADS, IDX_DIM, MLA_HEADS, MLA_DIM, MLA_DV, MAX_TOPK = 64, 64, 12
 EXPORTS = ["dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
            "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
            "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc",
+           "dsa_masked_mha_prefill",
            "dsa_workspace_size", "dsa_default_splits", "dsa_status_string", "dsa_last_error",
            "dsa_device_check", "dsa_device_checks_enabled",
            # measurement kernels (include/dsa_bench.h)
@@ -124,9 +126,11 @@ def _load(path: str) -> ctypes.CDLL:
     L.dsa_decode_step_noalloc.argtypes = [bp, ctypes.POINTER(dsa_indexer_inputs_t),
                                           ctypes.POINTER(dsa_mla_inputs_t), i32,
                                           ctypes.POINTER(dsa_step_opts_t), vp, vp, vp, vp]
+    L.dsa_masked_mha_prefill.argtypes = [bp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_decode_step",
               "dsa_cache_append", "dsa_topk_transform", "dsa_sparse_mla_decode_paged",
-              "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc"):
+              "dsa_decode_layers", "dsa_dense_mla_decode", "dsa_decode_step_noalloc",
+              "dsa_masked_mha_prefill"):
         getattr(L, f).restype = ctypes.c_int
     L.dsa_workspace_size.argtypes = [ctypes.c_int, bp, i32, i32]
     L.dsa_workspace_size.restype = sz
@@ -259,6 +263,14 @@ def dsa_sparse_mla_decode_paged(batch: Batch, q, kv_cache, slots, k: int, sm_sca
                                              int(k), float(sm_scale), _ptr(out), _ptr(lse),
                                              int(n_split), _ptr(ws), int(ws_bytes),
                                              _stream(stream)))
+
+
+def dsa_masked_mha_prefill(batch: Batch, q_nope, q_rope, w_uk, w_uv, kv_cache, idx, k: int,
+                           sm_scale: float, out, lse, ws, ws_bytes: int, stream=None):
+    _check(lib().dsa_masked_mha_prefill(batch.ref(), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                        _ptr(w_uv), _ptr(kv_cache), _ptr(idx), int(k),
+                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                        int(ws_bytes), _stream(stream)))
 
 
 def dsa_dense_mla_decode(batch: Batch, q, kv_cache, sm_scale: float, out, lse, n_split: int, ws,

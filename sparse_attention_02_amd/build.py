@@ -13,8 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 LIB_CHECKED = os.path.join(PKG, "libdsa_checked.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip",
-           "bench_kernels.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "mha_prefill.hip",
+           "cache_append.hip", "bench_kernels.hip"]
 # per-file code-generation options: the indexer reads its MFMA results with
 # VALU right away, so they are kept in VGPRs instead of AGPRs
 FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

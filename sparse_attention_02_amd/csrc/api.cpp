@@ -337,6 +337,8 @@ size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int32_t k, int32_t n
     case DSA_OP_DECODE_STEP:
       if (resolve_splits(batch, k, n_split, &used) != DSA_OK) return 0;
       return step_layout(batch, used).total;
+    case DSA_OP_MASKED_MHA:
+      return dsa::mha_supported(a) ? dsa::mha_ws_layout(a).total : 0;
     case DSA_OP_DENSE_MLA:
       if (resolve_splits(batch, std::max(1, batch->max_seqlen_k), n_split, &used) != DSA_OK ||
           used > dsa::kMaxSplits)
@@ -464,6 +466,33 @@ int dsa_dense_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint
                          size_t ws_bytes, void* stream) {
   return mla_common(batch, q, kv_cache, nullptr, 0, sm_scale, out, lse, n_split, ws, ws_bytes,
                     stream, dsa::kMlaDense);
+}
+
+int dsa_masked_mha_prefill(const dsa_batch_t* batch, const uint16_t* q_nope,
+                           const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv,
+                           const uint16_t* kv_cache, const int32_t* idx, int32_t k,
+                           float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err.clear();
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (idx && (k < 1 || k > DSA_MAX_TOPK)) return fail(DSA_ERR_INVALID_ARG, "k must be in [1, 8192]");
+  const dsa::BatchArgs a = launch_args(*batch);
+  if (!dsa::mha_supported(a))
+    return fail(DSA_ERR_UNSUPPORTED, "the masked MHA form covers at most 65536 tokens per row");
+  if (batch->num_tokens == 0) return DSA_OK;
+  if (!q_nope || !q_rope || !w_uk || !w_uv || !out ||
+      (!kv_cache && batch->max_seqlen_k > 0))
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16(q_nope) || misaligned16(q_rope) || misaligned16(w_uk) || misaligned16(w_uv) ||
+      misaligned16(kv_cache) || misaligned16(out) || misaligned16(ws))
+    return fail(DSA_ERR_INVALID_ARG, "q_nope, q_rope, w_uk, w_uv, kv_cache, out and ws need "
+                                     "16-byte alignment");
+  const size_t need = dsa::mha_ws_layout(a).total;
+  if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "masked MHA workspace too small");
+  hipError_t e = dsa::launch_masked_mha(a, q_nope, q_rope, w_uk, w_uv, kv_cache, idx, idx ? k : 0,
+                                        sm_scale, out, lse, ws, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "masked MHA launch");
 }
 
 int dsa_sparse_mla_decode_paged(const dsa_batch_t* batch, const uint16_t* q,

@@ -96,6 +96,20 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
 
 // idx[t, j] = j for j < v_t (j < k), -1 after: the selection of a row whose
 // visible tokens all fit in k.
+// Masked multi-head attention (expanded form): workspace of the expanded
+// keys and values [B][H][lp][128], the rope dims [B][lp][64] (bf16) and the
+// attend mask [T][lp/32] (lp: max_seqlen_k rounded up to 64).
+struct MhaWs {
+  size_t kn_off, vn_off, rope_off, mask_off, total;
+  int lp, nwords;
+};
+MhaWs mha_ws_layout(const BatchArgs& b);
+bool mha_supported(const BatchArgs& b);  // rows of at most 65536 positions
+hipError_t launch_masked_mha(const BatchArgs& b, const uint16_t* q_nope, const uint16_t* q_rope,
+                             const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* kv,
+                             const int32_t* idx, int k, float sm_scale, uint16_t* out,
+                             float* lse, void* ws, hipStream_t s);
+
 hipError_t launch_select_all(const BatchArgs& b, int k, int32_t* idx, hipStream_t s);
 
 }  // namespace dsa

@@ -46,6 +46,7 @@ SM_SCALE = 1.0 / math.sqrt(192.0)
 S_IDX_Q, S_W, S_KEYS, S_PERM, S_LENS, S_NOISE = 1, 2, 3, 5, 9, 8
 S_MLA_Q, S_KV = 6, 7  # + 16 * layer
 S_HEAVY = 0x100  # + request
+S_QN, S_QR, S_WUK, S_WUV = 0x201, 0x202, 0x203, 0x204  # expanded-form inputs
 
 
 def build(force: bool = False) -> str:
@@ -257,6 +258,17 @@ def make_batch(n_q, L, *, seed: int, paging: str = "identity", heavy=64, layers:
             batch.kv.append(bf16_normal(seed, S_KV + 16 * layer, (num_pages, PAGE, MLA_DIM),
                                         mla_scale, threads))
     return batch
+
+
+def mha_inputs(seed: int, T: int, q_std: float = 1.0, w_std: float = 1.0, threads: int = 0):
+    """Inputs of the expanded multi-head form as bf16 bits: q_nope [T, 128,
+    128] and q_rope [T, 128, 64] with standard deviation q_std, and the key
+    and value up-projections w_uk, w_uv [128, 128, 512] with w_std."""
+    qn = bf16_normal(seed, S_QN, (T, MLA_HEADS, 128), q_std, threads)
+    qr = bf16_normal(seed, S_QR, (T, MLA_HEADS, 64), q_std, threads)
+    wk = bf16_normal(seed, S_WUK, (MLA_HEADS, 128, 512), w_std, threads)
+    wv = bf16_normal(seed, S_WUV, (MLA_HEADS, 128, 512), w_std, threads)
+    return qn, qr, wk, wv
 
 
 # The five workloads.  Seeds: 0 for the single-request case, the workload's

@@ -216,6 +216,34 @@ def test_dense_mla_argument_checks(L):
         B.DSA_ERR_UNSUPPORTED
 
 
+def test_masked_mha_argument_checks(L):
+    P = 0x1000
+    b = _batch()  # B = 2, T = 4, max_seqlen_k = 300
+    need = L.dsa_workspace_size(B.DSA_OP_MASKED_MHA, ctypes.byref(b), 1, 0)
+    lp = 320  # 300 rounded up to 64
+    assert need >= 2 * 128 * lp * 128 * 2 * 2 + 2 * lp * 64 * 2 + 4 * (lp // 32) * 4
+    ok = (ctypes.byref(b), P, P, P, P, P, P, 64, 0.1, P, None, P, need, None)
+    for i in (1, 2, 3, 4, 9):  # each required pointer NULL in turn
+        args = list(ok)
+        args[i] = None
+        assert L.dsa_masked_mha_prefill(*args) == B.DSA_ERR_INVALID_ARG, i
+    args = list(ok)
+    args[1] = P + 8  # q_nope off the 16-byte grid
+    assert L.dsa_masked_mha_prefill(*args) == B.DSA_ERR_INVALID_ARG
+    args = list(ok)
+    args[7] = 0  # k with a selection
+    assert L.dsa_masked_mha_prefill(*args) == B.DSA_ERR_INVALID_ARG
+    args = list(ok)
+    args[12] = need - 1
+    assert L.dsa_masked_mha_prefill(*args) == B.DSA_ERR_WORKSPACE
+    long = _batch(max_seqlen_k=65537, max_pages=1025)
+    assert L.dsa_workspace_size(B.DSA_OP_MASKED_MHA, ctypes.byref(long), 1, 0) == 0
+    args = list(ok)
+    args[0] = ctypes.byref(long)
+    args[12] = 1 << 40
+    assert L.dsa_masked_mha_prefill(*args) == B.DSA_ERR_UNSUPPORTED
+
+
 def test_sparse_mla_argument_checks(L):
     P = 0x1000
     b = _batch()
