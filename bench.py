@@ -24,7 +24,9 @@ two-stream multi-layer-indexer step on a ragged 48-request batch (selection
 overlap of adjacent layers, time against the one-stream step), the layer
 stack, the short-context form, cache appends, index spaces, the gathered
 bytes counted once per request, and the single-request step (1 row onto
-8192 tokens) warm and cold.  --prefill-only times just the prefill form.
+8192 tokens) warm and cold.  --prefill-only times just the prefill form;
+--short-prefill-only just the 4096-row prefill on an empty cache (the sparse
+step against the masked multi-head step).
 """
 from __future__ import annotations
 
@@ -743,6 +745,9 @@ def main():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill-chunk form (for counter runs) and print it")
+    ap.add_argument("--short-prefill-only", action="store_true",
+                    help="time only the 4096-row prefill on an empty cache (sparse step, masked "
+                         "multi-head step, dense absorbed attention) and print it")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-mfma", metavar="DIR")
@@ -768,6 +773,9 @@ def main():
     dsa.lib()
     if args.prefill_only:
         print(json.dumps(prefill_measure(args.steps)), flush=True)
+        return
+    if args.short_prefill_only:
+        print(json.dumps(short_prefill_measure(max(3, args.steps // 10))), flush=True)
         return
     t0 = time.perf_counter()
     b = synth.make_workload(DECODE_WORKLOAD)
