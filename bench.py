@@ -18,13 +18,15 @@ algorithmic bytes over the average of those per-launch durations.
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR   (two rocprofv3 --pmc runs)
   python bench.py --summarize-mfma DIR     (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE)
 
---extras adds more measurements to the line: the prefill-chunk form
-(4096 query rows on a 61440-token prefix: indexer FP8 MFMA utilisation), the
-two-stream multi-layer-indexer step on a ragged 48-request batch (selection
-overlap of adjacent layers, time against the one-stream step), the layer
-stack, the short-context form, cache appends, index spaces, the gathered
-bytes counted once per request, and the single-request step (1 row onto
-8192 tokens) warm and cold.  --prefill-only times just the prefill form;
+The line also carries the 32-request 32K-context decode batch, the
+4096-row prefill on an empty cache (the sparse step against the masked
+multi-head form), and the single-request step (1 row onto 8192 tokens)
+warm and cold.  --extras adds more: the prefill-chunk form (4096 query rows
+on a 61440-token prefix: indexer FP8 MFMA utilisation), the two-stream
+multi-layer-indexer step on a ragged 48-request batch (selection overlap of
+adjacent layers, time against the one-stream step), the layer stack, the
+short-context form, cache appends, index spaces and the gathered bytes
+counted once per request.  --prefill-only times just the prefill form;
 --short-prefill-only just the 4096-row prefill on an empty cache (the sparse
 step against the masked multi-head step).
 """
@@ -806,6 +808,12 @@ def main():
     b32 = decode_b32_measure(max(20, args.steps // 2))
     log(f"{b32['workload']}: step {b32['ms_per_step']:.3f} ms, "
         f"{b32['query_tokens_per_s']:.0f} query-tokens/s, {b32['achieved_gbs']:.0f} GB/s")
+    # the 4096-row prefill on an empty cache: sparse step against the masked
+    # multi-head form; and the single-request latency workload
+    short_prefill = short_prefill_measure(max(3, args.steps // 20))
+    log(f"short prefill {short_prefill}")
+    latency = latency_measure()
+    log(f"single-request latency {latency}")
 
     result = {
         "metric": METRIC,
@@ -838,6 +846,8 @@ def main():
                                "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": attn_gbs / HBM_PEAK_GBS},
         "decode_b32_mtp1_ctx32768": b32,
+        "short_prefill": short_prefill,
+        "latency": latency,
     }
     if args.extras:
         result["prefill"] = prefill_measure(max(3, args.steps // 10))
@@ -846,15 +856,11 @@ def main():
         log(f"mli {result['mli']}")
         result["short_context"] = short_measure(max(5, args.steps // 2))
         log(f"short context {result['short_context']}")
-        result["short_prefill"] = short_prefill_measure(max(3, args.steps // 10))
-        log(f"short prefill {result['short_prefill']}")
         result["cache_append"] = append_measure()
         log(f"cache append {result['cache_append']}")
         result["index_space"] = space
         result["step_hbm"]["gathered_bytes_union"] = union
         result["step_hbm"]["gathered_bytes_per_row"] = work["attention_gather_bytes"]
-        result["latency"] = latency_measure()
-        log(f"single-request latency {result['latency']}")
         log(f"top-k + attention, logical vs physical-slot indices {result['index_space']}")
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
