@@ -204,9 +204,10 @@ __global__ __launch_bounds__(kMaskThreads) void mha_mask_kernel(BatchArgs b,
 // 64 positions pass through LDS, double-buffered, by DMA (global_load_lds):
 // K (64 x 128 dims, 16 KB), rope (64 x 64 dims, 8 KB) and V (64 x 128, 16
 // KB).  Row chunks are XOR-swizzled so that the operand reads (16 rows at
-// one 16-byte column) are free of bank conflicts: chunk c of K or V row r
-// sits at chunk c ^ (r & 15) of the row, chunk c of rope row r at c ^ ((r >>
-// 1) & 7).  Per 32-key half tile:
+// one 16-byte column) and the transposing V reads are free of bank
+// conflicts: chunk c of K or V row r sits at chunk c ^ kv_swz(r) of the row
+// (with c ^ (r & 15) the V reads conflicted two-way: 28 % of the LDS time),
+// chunk c of rope row r at c ^ ((r >> 1) & 7).  Per 32-key half tile:
 //   S^T   = K Q^T (keys x queries, 6 k-steps of 32 dims: 4 of K, 2 of rope),
 //           the wave's queries held in registers as B operands;
 //   softmax online per query in fp32, with the mask bits; the reference max
@@ -215,8 +216,9 @@ __global__ __launch_bounds__(kMaskThreads) void mha_mask_kernel(BatchArgs b,
 //           transposing LDS reads in the token order the accumulators use.
 // Each wave owns its queries' outputs (128 dims), so no data crosses waves
 // but the K/V tiles.
-constexpr int kAttThreads = 256;
-constexpr int kQBlk = 128;    // query rows per work-group
+constexpr int kAttWaves = 4;
+constexpr int kAttThreads = 64 * kAttWaves;
+constexpr int kQBlk = 32 * kAttWaves;  // query rows per work-group (32 per wave)
 constexpr int kKTile = 64;    // keys per tile
 constexpr int kKnBytes = kKTile * kDn * 2;   // 16 KB
 constexpr int kRBytes = kKTile * kDr * 2;    // 8 KB
@@ -231,6 +233,12 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0); lgkmcnt(0)
 constexpr unsigned kWaitVmAll = 0x0f70;
 constexpr unsigned kWaitLgkmAll = 0xc07f;
+
+// Chunk c (16 bytes) of K or V row r sits at chunk c ^ kv_swz(r) of the row.
+// The 16 rows of an operand read (rows r .. r+15 at one chunk) land on 16
+// distinct chunks, and so do the two-chunk pieces of 8 consecutive rows that
+// one half of a transposing V read covers: both free of bank conflicts.
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -295,18 +303,18 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
   // DMA of tile `tile` into stage `st`: 16 + 8 + 16 wave-wide 1 KB loads,
   // 10 per wave.  Load i of K (or V) fills LDS bytes 1024 i .. +1023 = rows
   // 4i .. 4i+3; lane L writes LDS chunk L % 16 of row 4i + L / 16 and so
-  // reads global chunk (L % 16) ^ (row & 15).  Rope load i covers rows 8i ..
+  // reads global chunk (L % 16) ^ kv_swz(row).  Rope load i covers rows 8i ..
   // 8i+7, lane L chunk L % 8 of row 8i + L / 8, from chunk (L % 8) ^ ((row >>
   // 1) & 7).
   const uint16_t* kn_h = kn + ((int64_t)bi * kH + h) * lp * kDn;
   const uint16_t* vn_h = vn + ((int64_t)bi * kH + h) * lp * kDn;
   const uint16_t* rp_b = rope + (int64_t)bi * lp * kDr;
   // A wave's loads are K/V loads i = wave + 4u and rope loads i = wave + 4u -
-  // 16: row & 15 (K, V) and (row >> 1) & 7 (rope) do not depend on u, so
+  // 16: kv_swz(row) (K, V) and (row >> 1) & 7 (rope) do not depend on u, so
   // each lane's byte offset within a load's rows is the same for all of
   // them and only the scalar base moves.
   const int kv_row = 4 * wave + (lane >> 4);  // row of the wave's first K/V load
-  const uint32_t kv_off = (uint32_t)(kv_row * (kDn * 2) + 16 * ((lane & 15) ^ (kv_row & 15)));
+  const uint32_t kv_off = (uint32_t)(kv_row * (kDn * 2) + 16 * ((lane & 15) ^ kv_swz(kv_row)));
   const int r_row = 8 * wave + (lane >> 3);   // row of the wave's first rope load (mod 32)
   const uint32_t r_off = (uint32_t)((lane >> 3) * (kDr * 2) + 16 * ((lane & 7) ^ ((r_row >> 1) & 7)));
   const unsigned char* kn_b = reinterpret_cast<const unsigned char*>(kn_h);
@@ -315,11 +323,11 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
   auto issue_tile = [&](int tile, int st) {
     const int64_t key0 = (int64_t)tile * kKTile;
 #pragma unroll
-    for (int u = 0; u < 10; ++u) {
-      const int i = wave + 4 * u;  // 0..39: K loads 0..15, rope 16..23, V 24..39
+    for (int u = 0; u < 40 / kAttWaves; ++u) {
+      const int i = wave + kAttWaves * u;  // 0..39: K loads 0..15, rope 16..23, V 24..39
       if (i < 16) {
-        // rows 4i .. 4i+3 = kv_row - 4 wave + 4i + (0 .. 3 by lane): base row 16u
-        __builtin_amdgcn_global_load_lds(kn_b + (key0 + 16 * u) * (kDn * 2) + kv_off,
+        // rows 4i .. 4i+3: base row 4i - 4 wave (= 4 kAttWaves u)
+        __builtin_amdgcn_global_load_lds(kn_b + (key0 + 4 * (i - wave)) * (kDn * 2) + kv_off,
                                          Kn[st] + 1024 * i, 16, 0, 0);
       } else if (i < 24) {
         const int ii = i - 16;
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
                                          Rp[st] + 1024 * ii, 16, 0, 0);
       } else {
         const int ii = i - 24;
-        // rows 4 ii .. 4 ii + 3: base row 4 ii - 4 wave (= 16u - 96)
+        // rows 4 ii .. 4 ii + 3: base row 4 ii - 4 wave
         __builtin_amdgcn_global_load_lds(vn_b + (key0 + 4 * (ii - wave)) * (kDn * 2) + kv_off,
                                          Vn[st] + 1024 * ii, 16, 0, 0);
       }
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
         for (int e = 0; e < 2; ++e) {
           const int row = kb0 + 16 * e + l16;
           if (kk < 4) {
-            const int ch = (4 * kk + g) ^ (row & 15);
+            const int ch = (4 * kk + g) ^ kv_swz(row);
             a[e] = as_frag(*reinterpret_cast<const uint4*>(K + row * (kDn * 2) + 16 * ch));
           } else {
             const int ch = (4 * (kk - 4) + g) ^ ((row >> 1) & 7);
@@ -459,9 +467,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
         const int row = kb0 + 4 * g + (l16 >> 2);
         const int dim = 16 * db + 4 * (l16 & 3);
         const int ch = dim >> 3, sub = (dim & 7) * 2;
-        const unsigned char* p_lo = V + row * (kDn * 2) + 16 * (ch ^ (row & 15)) + sub;
-        const unsigned char* p_hi =
-            V + (row + 16) * (kDn * 2) + 16 * (ch ^ ((row + 16) & 15)) + sub;
+        const unsigned char* p_lo = V + row * (kDn * 2) + 16 * (ch ^ kv_swz(row)) + sub;
+        const unsigned char* p_hi = V + (row + 16) * (kDn * 2) + 16 * (ch ^ kv_swz(row + 16)) + sub;
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p_lo));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p_hi));
         const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
