@@ -205,8 +205,7 @@ __global__ __launch_bounds__(kMaskThreads) void mha_mask_kernel(BatchArgs b,
 // K (64 x 128 dims, 16 KB), rope (64 x 64 dims, 8 KB) and V (64 x 128, 16
 // KB).  Row chunks are XOR-swizzled so that the operand reads (16 rows at
 // one 16-byte column) and the transposing V reads are free of bank
-// conflicts: chunk c of K or V row r sits at chunk c ^ kv_swz(r) of the row
-// (with c ^ (r & 15) the V reads conflicted two-way: 28 % of the LDS time),
+// conflicts: chunk c of K or V row r sits at chunk c ^ kv_swz(r) of the row,
 // chunk c of rope row r at c ^ ((r >> 1) & 7).  Per 32-key half tile:
 //   S^T   = K Q^T (keys x queries, 6 k-steps of 32 dims: 4 of K, 2 of rope),
 //           the wave's queries held in registers as B operands;
