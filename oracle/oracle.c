@@ -415,6 +415,7 @@ typedef struct {
   int32_t k;
   double sm_scale;
   const int32_t* rows;
+  int32_t n_rows;
   double* out;
   double* lse;
   int64_t num_pages;
@@ -422,71 +423,107 @@ typedef struct {
 
 enum { MHA_DN = 128, MHA_DR = 64, MHA_C = 512, MHA_KV = 576 };
 
+/* One item = (request b, head h): the up-projected keys and values of the
+ * request's positions are formed once, then every requested row of b
+ * attends over its positions. */
 static void mha_item(void* p, int64_t item) {
   mha_ctx* c = (mha_ctx*)p;
-  int64_t i = item / c->H;
+  int32_t b = (int32_t)(item / c->H);
   int32_t h = (int32_t)(item % c->H);
-  int32_t t = c->rows[i];
-  int32_t b = oracle_row_request(c->bt, t);
-  int64_t v = b < 0 ? 0 : oracle_row_visible(c->bt, t);
-  double* o = c->out + (i * c->H + h) * MHA_DN;
-  for (int d = 0; d < MHA_DN; ++d) o[d] = 0.0;
-  int64_t n = 0;
-  int64_t cap = c->idx ? c->k : v;
-  int64_t* S = (int64_t*)malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
-  if (c->idx) {
-    for (int32_t j = 0; j < c->k; ++j) {
-      int32_t s = c->idx[i * c->k + j];
-      if (s >= 0 && s < v && oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
+  /* the positions any requested row of b can see */
+  int64_t vmax = 0;
+  for (int32_t i = 0; i < c->n_rows; ++i)
+    if (oracle_row_request(c->bt, c->rows[i]) == b) {
+      int64_t v = oracle_row_visible(c->bt, c->rows[i]);
+      if (v > vmax) vmax = v;
     }
-  } else {
-    for (int64_t s = 0; s < v; ++s)
-      if (oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
-  }
-  if (n == 0) {
-    c->lse[i * c->H + h] = -INFINITY;
-    free(S);
+  if (vmax == 0) {
+    for (int32_t i = 0; i < c->n_rows; ++i)
+      if (oracle_row_request(c->bt, c->rows[i]) == b) {
+        double* o = c->out + ((int64_t)i * c->H + h) * MHA_DN;
+        for (int d = 0; d < MHA_DN; ++d) o[d] = 0.0;
+        c->lse[(int64_t)i * c->H + h] = -INFINITY;
+      }
     return;
   }
-  double qn[MHA_DN], qr[MHA_DR];
-  for (int d = 0; d < MHA_DN; ++d)
-    qn[d] = oracle_bf16_decode(c->qn[((int64_t)t * c->H + h) * MHA_DN + d]);
-  for (int r = 0; r < MHA_DR; ++r)
-    qr[r] = oracle_bf16_decode(c->qr[((int64_t)t * c->H + h) * MHA_DR + r]);
-  const uint16_t* wk = c->w_uk + (int64_t)h * MHA_DN * MHA_C;
-  const uint16_t* wv = c->w_uv + (int64_t)h * MHA_DN * MHA_C;
-  double* z = (double*)malloc(sizeof(double) * (size_t)n);
-  double* vn = (double*)malloc(sizeof(double) * (size_t)n * MHA_DN);
+  double* wk = (double*)malloc(sizeof(double) * MHA_DN * MHA_C);
+  double* wv = (double*)malloc(sizeof(double) * MHA_DN * MHA_C);
+  for (int64_t x = 0; x < (int64_t)MHA_DN * MHA_C; ++x) {
+    wk[x] = oracle_bf16_decode(c->w_uk[(int64_t)h * MHA_DN * MHA_C + x]);
+    wv[x] = oracle_bf16_decode(c->w_uv[(int64_t)h * MHA_DN * MHA_C + x]);
+  }
+  /* kn, vn, rope of positions 0 .. vmax-1 (unused for a page outside the pool) */
+  double* kn = (double*)calloc((size_t)vmax * MHA_DN, sizeof(double));
+  double* vn = (double*)calloc((size_t)vmax * MHA_DN, sizeof(double));
+  double* rp = (double*)calloc((size_t)vmax * MHA_DR, sizeof(double));
   double lat[MHA_C];
-  double m = -INFINITY;
-  for (int64_t j = 0; j < n; ++j) {
-    const uint16_t* row = c->kv + oracle_slot(c->bt, b, S[j]) * MHA_KV;
+  for (int64_t s = 0; s < vmax; ++s) {
+    if (!oracle_page_valid(c->bt, b, s, c->num_pages)) continue;
+    const uint16_t* row = c->kv + oracle_slot(c->bt, b, s) * MHA_KV;
     for (int x = 0; x < MHA_C; ++x) lat[x] = oracle_bf16_decode(row[x]);
-    double dot = 0.0;
     for (int d = 0; d < MHA_DN; ++d) {
-      double kn = 0.0, vv = 0.0;
+      double a = 0.0, v = 0.0;
       for (int x = 0; x < MHA_C; ++x) {
-        kn += oracle_bf16_decode(wk[d * MHA_C + x]) * lat[x];
-        vv += oracle_bf16_decode(wv[d * MHA_C + x]) * lat[x];
+        a += wk[d * MHA_C + x] * lat[x];
+        v += wv[d * MHA_C + x] * lat[x];
       }
-      dot += qn[d] * kn;
-      vn[j * MHA_DN + d] = vv;
+      kn[s * MHA_DN + d] = a;
+      vn[s * MHA_DN + d] = v;
     }
-    for (int r = 0; r < MHA_DR; ++r) dot += qr[r] * oracle_bf16_decode(row[MHA_C + r]);
-    z[j] = c->sm_scale * dot;
-    if (z[j] > m) m = z[j];
+    for (int r = 0; r < MHA_DR; ++r) rp[s * MHA_DR + r] = oracle_bf16_decode(row[MHA_C + r]);
   }
-  double sum = 0.0;
-  for (int64_t j = 0; j < n; ++j) {
-    z[j] = exp(z[j] - m);
-    sum += z[j];
+  int64_t* S = (int64_t*)malloc(sizeof(int64_t) * (size_t)(vmax > c->k ? vmax : c->k));
+  double* z = (double*)malloc(sizeof(double) * (size_t)(vmax > c->k ? vmax : c->k));
+  for (int32_t i = 0; i < c->n_rows; ++i) {
+    int32_t t = c->rows[i];
+    if (oracle_row_request(c->bt, t) != b) continue;
+    int64_t v = oracle_row_visible(c->bt, t);
+    double* o = c->out + ((int64_t)i * c->H + h) * MHA_DN;
+    for (int d = 0; d < MHA_DN; ++d) o[d] = 0.0;
+    /* the position list S */
+    int64_t n = 0;
+    if (c->idx) {
+      for (int32_t j = 0; j < c->k; ++j) {
+        int32_t s = c->idx[(int64_t)i * c->k + j];
+        if (s >= 0 && s < v && oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
+      }
+    } else {
+      for (int64_t s = 0; s < v; ++s)
+        if (oracle_page_valid(c->bt, b, s, c->num_pages)) S[n++] = s;
+    }
+    if (n == 0) {
+      c->lse[(int64_t)i * c->H + h] = -INFINITY;
+      continue;
+    }
+    double qn[MHA_DN], qr[MHA_DR];
+    for (int d = 0; d < MHA_DN; ++d)
+      qn[d] = oracle_bf16_decode(c->qn[((int64_t)t * c->H + h) * MHA_DN + d]);
+    for (int r = 0; r < MHA_DR; ++r)
+      qr[r] = oracle_bf16_decode(c->qr[((int64_t)t * c->H + h) * MHA_DR + r]);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < MHA_DN; ++d) dot += qn[d] * kn[S[j] * MHA_DN + d];
+      for (int r = 0; r < MHA_DR; ++r) dot += qr[r] * rp[S[j] * MHA_DR + r];
+      z[j] = c->sm_scale * dot;
+      if (z[j] > m) m = z[j];
+    }
+    double sum = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      z[j] = exp(z[j] - m);
+      sum += z[j];
+    }
+    for (int64_t j = 0; j < n; ++j)
+      for (int d = 0; d < MHA_DN; ++d) o[d] += z[j] / sum * vn[S[j] * MHA_DN + d];
+    c->lse[(int64_t)i * c->H + h] = m + log(sum);
   }
-  for (int64_t j = 0; j < n; ++j)
-    for (int d = 0; d < MHA_DN; ++d) o[d] += z[j] / sum * vn[j * MHA_DN + d];
-  c->lse[i * c->H + h] = m + log(sum);
-  free(vn);
   free(z);
   free(S);
+  free(rp);
+  free(vn);
+  free(kn);
+  free(wv);
+  free(wk);
 }
 
 void oracle_masked_mha(const oracle_batch* bt, int64_t num_pages, int32_t H, const uint16_t* qn,
@@ -494,8 +531,8 @@ void oracle_masked_mha(const oracle_batch* bt, int64_t num_pages, int32_t H, con
                        const uint16_t* kv, const int32_t* idx, int32_t k, double sm_scale,
                        const int32_t* rows, int32_t n_rows, double* out, double* lse,
                        int threads) {
-  mha_ctx c = {bt, H, qn, qr, w_uk, w_uv, kv, idx, k, sm_scale, rows, out, lse, num_pages};
-  run_items((int64_t)n_rows * H, threads, mha_item, &c);
+  mha_ctx c = {bt, H, qn, qr, w_uk, w_uv, kv, idx, k, sm_scale, rows, n_rows, out, lse, num_pages};
+  run_items((int64_t)bt->B * H, threads, mha_item, &c);
 }
 
 /* ---- cache append ---------------------------------------------------------
