@@ -186,6 +186,23 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const int g = lane >> 4;
   const int head = wave * 16 + l16;
 
+  // B operand of S^T: q[t, head, 32kk + 8g .. +8]; the latent part in
+  // registers, the rope part (k-steps 16 and 17) in LDS
+  v8bf qf[16];
+  uint4 qr_pre[2];
+  {
+    const uint4* src =
+        reinterpret_cast<const uint4*>(q + ((int64_t)t * DSA_MLA_HEADS + head) * DSA_MLA_DIM) + g;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      Frag f;
+      f.u = src[4 * kk];
+      qf[kk] = f.v;
+    }
+    qr_pre[0] = src[4 * 16];
+    qr_pre[1] = src[4 * 17];
+  }
+
   // position -> slot for the whole split (-1: skipped); paged entries are
   // slots already (only their range is checked); the dense form attends
   // every visible position, the entry being the position itself
@@ -207,23 +224,12 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     }
     slots[i] = slot;
   }
+  // the query loads and the slot table's loads overlapped; all have landed
+  // before the first gather is issued
+  wait_vm_all();
+  Qr[0][wave * 64 + lane] = qr_pre[0];
+  Qr[1][wave * 64 + lane] = qr_pre[1];
   __syncthreads();
-
-  // B operand of S^T: q[t, head, 32kk + 8g .. +8]; the latent part in
-  // registers, the rope part (k-steps 16 and 17) in LDS
-  v8bf qf[16];
-  {
-    const uint4* src =
-        reinterpret_cast<const uint4*>(q + ((int64_t)t * DSA_MLA_HEADS + head) * DSA_MLA_DIM) + g;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      Frag f;
-      f.u = src[4 * kk];
-      qf[kk] = f.v;
-    }
-    Qr[0][wave * 64 + lane] = src[4 * 16];
-    Qr[1][wave * 64 + lane] = src[4 * 17];
-  }
 
   // slots of a tile, one per lane: lane L holds token L % 32 (-1: skipped or
   // past the split)
@@ -420,49 +426,61 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   const float lse_v = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   if (g == 0) fin_l[head] = l_tot > 0.f ? 1.f / l_tot : 0.f;
   lds_barrier();
-  // lane holds O^T[d_base + 16db + 4g + r][16hb + l16]
+  // lane holds O^T[d_base + 16db + 4g + r][16hb + l16].  The wave's 64
+  // dims of each head leave as one 128-byte row: four head blocks at a time
+  // are packed into an 8 KB LDS region of the wave (the ring is free now;
+  // 16-byte chunks XOR-swizzled by row), then read back 16 bytes a lane
+  // (eight lanes per row) and stored row by row.
+  unsigned char* stage_out = (wave < 4 ? Ks0 : Ks1) + (wave & 3) * 8192;
 #pragma unroll
-  for (int hb = 0; hb < 8; ++hb) {
-    const int h = 16 * hb + l16;
-    const float inv = fin_l[h];
-    if (!SPLIT) {
-      uint16_t* o = out + ((int64_t)t * DSA_MLA_HEADS + h) * DSA_MLA_DV + d_base + 4 * g;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int hq = 0; hq < 4; ++hq) {
+      const int hb = 4 * pass + hq;
+      const int h = 16 * hb + l16;
+      const float inv = fin_l[h];
+      float f = inv;
+      if (SPLIT) {
+        // the split's partial in fp16, scaled per (head, this wave's 64 dims)
+        // by a power of two that puts its largest magnitude in [2^14, 2^15):
+        // 11 significant bits, against 8 for the bf16 output
+        float mx = 0.f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[db][hb][r]));
+        {  // max over the four 16-lane rows, which hold the head's other dims
+          const v2u x = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+          mx = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+          const v2u y = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+          mx = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+        }
+        const float sc = half_scale(mx * inv);
+        f = inv * sc;
+        if (g == 0)
+          spart[(((int64_t)t * n_split + split) * (kThreads / 64) + wave) * DSA_MLA_HEADS + h] =
+              1.f / sc;
+      }
+      const int row = 16 * hq + l16;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const v4f x = acc[db][hb];
-        *reinterpret_cast<uint2*>(o + 16 * db) =
-            make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
+        const int c = (2 * db + (g >> 1)) ^ (row & 7);
+        *reinterpret_cast<uint2*>(stage_out + row * 128 + c * 16 + 8 * (g & 1)) =
+            SPLIT ? make_uint2(pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f))
+                  : make_uint2(pack_bf16x2(x[0] * f, x[1] * f), pack_bf16x2(x[2] * f, x[3] * f));
       }
-    } else {
-      // the split's partial in fp16, scaled per (head, this wave's 64 dims)
-      // by a power of two that puts its largest magnitude in [2^14, 2^15):
-      // 11 significant bits, against 8 for the bf16 output
-      float mx = 0.f;
+    }
+    uint16_t* dst = SPLIT ? opart + ((int64_t)t * n_split + split) * DSA_MLA_HEADS * DSA_MLA_DV
+                          : out + (int64_t)t * DSA_MLA_HEADS * DSA_MLA_DV;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[db][hb][r]));
-      {  // max over the four 16-lane rows, which hold the head's other dims
-        const v2u x = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-        mx = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
-        const v2u y = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-        mx = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
-      }
-      const float sc = half_scale(mx * inv);
-      uint16_t* o = opart + (((int64_t)t * n_split + split) * DSA_MLA_HEADS + h) * DSA_MLA_DV +
-                    d_base + 4 * g;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const v4f x = acc[db][hb];
-        const float f = inv * sc;
-        *reinterpret_cast<uint2*>(o + 16 * db) =
-            make_uint2(pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f));
-      }
-      if (g == 0)
-        spart[(((int64_t)t * n_split + split) * (kThreads / 64) + wave) * DSA_MLA_HEADS + h] =
-            1.f / sc;
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int cc = lane & 7;
+      const uint4 w = *reinterpret_cast<const uint4*>(stage_out + row * 128 + ((cc ^ (row & 7)) * 16));
+      *reinterpret_cast<uint4*>(dst + (int64_t)(64 * pass + row) * DSA_MLA_DV + d_base + 8 * cc) = w;
     }
   }
   if (g == 0) {
@@ -483,8 +501,12 @@ constexpr int kMergeWaves = 8;
 __global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(
     const uint16_t* __restrict__ opart, const float* __restrict__ spart,
     const float* __restrict__ lpart, int n_split, int64_t n_th, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
-  const int64_t th = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);  // t * 128 + h
+    float* __restrict__ lse, int per_xcd) {
+  // work-groups are dealt to the 8 XCDs round-robin; XCD x takes the x-th
+  // eighth of the (row, head) range, the rows whose splits the attention ran
+  // on that XCD, so the partials are read from the L2 that they were written to
+  const int64_t wg = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int64_t th = wg * kMergeWaves + (threadIdx.x >> 6);  // t * 128 + h
   if (th >= n_th) return;
   const int64_t t = th / DSA_MLA_HEADS;
   const int h = (int)(th - t * DSA_MLA_HEADS);
@@ -621,8 +643,10 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
                      idx, k, scale_log2, out, lse, opart, spart, lpart, used, chunk, n_work, per_xcd,
                      idx_mode);
   const int64_t n_th = (int64_t)b.T * DSA_MLA_HEADS;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)((n_th + kMergeWaves - 1) / kMergeWaves)),
-                     dim3(64 * kMergeWaves), 0, s, opart, spart, lpart, used, n_th, out, lse);
+  const int64_t n_mwg = (n_th + kMergeWaves - 1) / kMergeWaves;
+  const int m_per_xcd = (int)((n_mwg + 7) / 8);
+  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(8 * m_per_xcd)),
+                     dim3(64 * kMergeWaves), 0, s, opart, spart, lpart, used, n_th, out, lse, m_per_xcd);
   return hipGetLastError();
 }
 
