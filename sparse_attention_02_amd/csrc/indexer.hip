@@ -121,10 +121,15 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
   }
 
   // page i of the chunk (past the end: the last page again; bad ids read
-  // page 0 and score -inf)
+  // page 0 and score -inf).  The chunk's page ids are staged in LDS once, so
+  // a page's address costs an in-order LDS read rather than a scalar load
+  // (whose wait, scalar loads returning out of order, is always a full one).
   const int32_t* ptab = b.pages + (int64_t)bi * b.max_pages;
   const int lane_key = 16 * wave + j;
-  auto page_id = [&](int i) { return ptab[min(p_begin + i, p_end - 1)]; };
+  __shared__ int lpid[KC];
+  for (int i = threadIdx.x; i < KC; i += kThreads) lpid[i] = ptab[min(p_begin + i, p_end - 1)];
+  __syncthreads();
+  auto page_id = [&](int i) { return lpid[min(i, KC - 1)]; };
   auto page_ok = [&](int pg) { return pg >= 0 && pg < b.num_pages; };
   auto key_ptr = [&](int pg) {
     return k8 + (int64_t)(page_ok(pg) ? pg : 0) * (DSA_PAGE_SIZE * DSA_IDX_DIM) +
@@ -166,28 +171,37 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
   }
   float* srow = scores + (int64_t)(c0 + r0 + min(g, nr - 1)) * ld;
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  if (HIST) __syncthreads();
+  // (the staging barrier above also ordered the histogram's zeroing)
 
+  int pg_next = page_id(NPF);  // the page whose keys are loaded next
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     const v8i kcur = kf[i % NPF];
     const float kscur = ksr[i % NPF];
     if (i + NPF < KC) {
-      const int pg = page_id(i + NPF);
+      const int pg = pg_next;
+      pg_next = page_id(i + NPF + 1);
       kf[i % NPF] = NT ? load_frag_nt(key_ptr(pg)) : load_frag(key_ptr(pg));
       ksr[i % NPF] = *scale_ptr(pg);
     }
+    // the products of (row, head tile) x = 4 r + m, one ahead of the ReLU * w
+    // that reads them: two accumulators in turn, so each MFMA runs while the
+    // previous one's results are consumed (with one accumulator the next
+    // product waits for the reads, and the results for the product)
     float sum[RG];
+    v4f acc_cur =
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[0][0], kcur, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      sum[r] = 0.f;
+    for (int x = 0; x < 4 * RG; ++x) {
+      const int r = x >> 2, m = x & 3;
+      v4f acc_next = zero;
+      if (x + 1 < 4 * RG)
+        acc_next = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[(x + 1) >> 2][(x + 1) & 3],
+                                                                   kcur, zero, 0, 0, 0, 0, 0, 0);
+      if (m == 0) sum[r] = 0.f;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const v4f acc =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[r][m], kcur, zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum[r] = fmaf(wr[r][m][e], relu(acc[e]), sum[r]);
-      }
+      for (int e = 0; e < 4; ++e) sum[r] = fmaf(wr[r][m][e], relu(acc_cur[e]), sum[r]);
+      acc_cur = acc_next;
     }
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
