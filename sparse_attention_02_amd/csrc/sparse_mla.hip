@@ -32,7 +32,8 @@
 //            token order in which the S^T accumulator holds P.
 // With several splits per row each writes its normalised partial output in
 // fp16, scaled per (head, 64-dim slice) by a power of two, plus the slice
-// scales and its lse, and a merge kernel combines them.
+// scales and its lse, and a merge kernel combines them.  The output (or
+// partial) leaves through LDS as whole 128-byte rows of one head.
 // The loop is software-pipelined: step i runs the value product of tile i
 // and the scores of tile i+1 while tile i+2 streams in, with one barrier per
 // step.  Operand reads run ahead of the products that use them (two k-steps
