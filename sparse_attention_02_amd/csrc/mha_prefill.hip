@@ -53,7 +53,10 @@ __device__ __forceinline__ v8bf as_frag(uint4 u) {
 // positions, double-buffered: one 1 KB DMA per row (its 512 latent dims),
 // chunk c of row r stored at chunk c ^ (r & 15) so that the B-operand reads
 // (16 rows at one 16-byte column) are free of bank conflicts.  Each lane
-// ends with 4 consecutive dims of one position: one 8-byte store.
+// ends with 4 consecutive dims of one position: one 8-byte store.  A
+// block's slots and their validity come from its DMA issue (no page-table
+// loads before the stores), and the rope dims of block j are copied by the
+// work-groups of head j mod 128, so no head's work-groups carry all of it.
 constexpr int kExpPos = 64;
 constexpr int kExpThreads = 512;
 constexpr int kExpRow = kC * 2;  // 1024 bytes of latent per row in LDS
@@ -92,11 +95,16 @@ __global__ __launch_bounds__(kExpThreads, 1) void mha_expand_kernel(
   // 8; lane L fills LDS chunk L of the row from global chunk L ^ (r & 15).
   // Positions past the request or on a page outside the pool read slot 0 and
   // are stored as zeros.
+  // (the block's slots and their validity are kept for its stores and rope copy)
+  int slot_n = 0;
+  uint64_t ok_n = 0;
   auto issue = [&](int blk, int st) {
     const int s = blk * kExpPos + lane;
     const int64_t sl = s < L ? slot_of(b, bi, s) : -1;
     device_check(b, s < L && sl < 0, DSA_CHECK_PAGE_ID);
     const int my_slot = sl < 0 ? 0 : (int)sl;
+    slot_n = my_slot;
+    ok_n = __ballot(sl >= 0);
 #pragma unroll
     for (int i = 0; i < kExpPos / 8; ++i) {
       const int r = wave + 8 * i;
@@ -111,6 +119,8 @@ __global__ __launch_bounds__(kExpThreads, 1) void mha_expand_kernel(
   int st = 0;
   issue(share, 0);
   for (int blk = share; blk < nblk; blk += n_share, st ^= 1) {
+    const int slot_c = slot_n;   // slot of position 64 blk + lane (0: none)
+    const uint64_t ok_c = ok_n;  // bit r: position 64 blk + r is on a page in the pool
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's rows have landed
     __syncthreads();                     // every wave's have; the other stage is free
     if (blk + n_share < nblk) issue(blk + n_share, st ^ 1);
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(kExpThreads, 1) void mha_expand_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int s = blk * kExpPos + 16 * q + l16;
-      const bool ok = s < L && slot_of(b, bi, s) >= 0;
+      const bool ok = (ok_c >> (16 * q + l16)) & 1;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const v4f x = ok ? acc[db][q] : v4f{0.f, 0.f, 0.f, 0.f};
@@ -145,13 +155,16 @@ __global__ __launch_bounds__(kExpThreads, 1) void mha_expand_kernel(
             make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
       }
     }
-    if (h == 0) {
-      // the rope dims of the block's positions, 8 chunks of 16 bytes each
+    if (h == blk % kH) {
+      // the rope dims of the block's positions (one head's work-groups per
+      // block, spread over the heads), 8 chunks of 16 bytes each
       for (int i = tid; i < kExpPos * 8; i += kExpThreads) {
-        const int s = blk * kExpPos + i / 8, c = i % 8;
-        const int64_t sl = s < L ? slot_of(b, bi, s) : -1;
+        const int r = i / 8, c = i % 8;
+        const int s = blk * kExpPos + r;
+        const int sl = __shfl(slot_c, r);
         uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (sl >= 0) x = *reinterpret_cast<const uint4*>(kv + sl * DSA_MLA_DIM + kC + 8 * c);
+        if ((ok_c >> r) & 1)
+          x = *reinterpret_cast<const uint4*>(kv + (int64_t)sl * DSA_MLA_DIM + kC + 8 * c);
         *reinterpret_cast<uint4*>(rope + ((int64_t)bi * lp + s) * kDr + 8 * c) = x;
       }
     }
