@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15;
   const int g = lane >> 4;
 

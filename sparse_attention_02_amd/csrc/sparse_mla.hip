@@ -182,7 +182,7 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int head = wave * 16 + l16;
@@ -247,14 +247,13 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
   // same for the whole wave, so its address is a scalar base plus a fixed
   // lane offset (no per-lane address arithmetic); a skipped row re-reads a
   // valid one, so every row the products touch holds finite cache data.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t tail_ofs = 1024u + 4u * (uint32_t)lane;  // bytes 1024 .. 1151 of a row (lanes < 32)
   auto issue_gather = [&](int sv, uint32_t bits, unsigned char* dst) {
     if (bits == 0) return;
     const int fb = __builtin_amdgcn_readlane(sv, __builtin_ctz(bits));
 #pragma unroll
     for (int i = 0; i < kMlaTile / 8; ++i) {
-      const int r = 4 * wave_u + i;
+      const int r = 4 * wave + i;
       int slot = __builtin_amdgcn_readlane(sv, r);
       if (slot < 0) slot = fb;
       const uint16_t* row = kv + (int64_t)slot * DSA_MLA_DIM;
