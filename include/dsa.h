@@ -188,7 +188,9 @@ int dsa_topk_transform(const dsa_batch_t* batch, const float* scores, int64_t ld
  *           scaled scores (-inf for a row with no valid entry)
  *  n_split  KV splits per row (0 = choose), 1 .. 64
  *  ws       workspace (>= dsa_workspace_size(DSA_OP_SPARSE_MLA, ...))
- * q, kv_cache, out and ws must be 16-byte aligned.
+ * q, kv_cache, out and ws must be 16-byte aligned.  q and the attended cache
+ * rows must hold no NaN (the kernels are compiled on that assumption): with
+ * one, out and lse are unspecified.
  * Errors: INVALID_ARG (also for misalignment), WORKSPACE. */
 int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint16_t* kv_cache,
                           const int32_t* idx, int32_t k, float sm_scale, uint16_t* out,
@@ -250,7 +252,8 @@ int dsa_dense_mla_decode(const dsa_batch_t* batch, const uint16_t* q, const uint
  *  ws       >= dsa_workspace_size(DSA_OP_MASKED_MHA, batch, k, 0) bytes:
  *           B * 128 * lp * 512 + B * lp * 128 + T * lp / 8 bytes, lp =
  *           max_seqlen_k rounded up to 64
- * Every pointer 16-byte aligned.
+ * Every pointer 16-byte aligned.  No input may hold a NaN (as for
+ * dsa_sparse_mla_decode): with one, out and lse are unspecified.
  * Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED (max_seqlen_k > 65536). */
 int dsa_masked_mha_prefill(const dsa_batch_t* batch, const uint16_t* q_nope,
                            const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv,

@@ -16,8 +16,15 @@ LIB_CHECKED = os.path.join(PKG, "libdsa_checked.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "mha_prefill.hip",
            "cache_append.hip", "bench_kernels.hip"]
 # per-file code-generation options: the indexer reads its MFMA results with
-# VALU right away, so they are kept in VGPRs instead of AGPRs
-FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# VALU right away, so they are kept in VGPRs instead of AGPRs.  The attention
+# kernels take maxima of MFMA results for their softmax; compiled assuming no
+# NaN values, each maximum is one v_max (or one v_max3 for three) instead of
+# also quieting both operands first (about 60 VALU per 64-key tile in the
+# masked multi-head loop).  Their inputs must hold no NaN: for one that does,
+# the outputs are unspecified.
+_NO_NANS = ["-fno-honor-nans"]
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "sparse_mla.hip": _NO_NANS, "mha_prefill.hip": _NO_NANS}
 HEADERS = ["internal.h", "device_common.h"]
 ARCH = "gfx950"
 

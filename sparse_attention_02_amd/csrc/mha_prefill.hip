@@ -19,6 +19,7 @@
 //            LDS, 128 query rows of one head per work-group.
 #include <algorithm>
 #include <cfloat>
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kMaskThreads) void mha_mask_kernel(BatchArgs b,
 //
 // Work-group: 4 waves, 128 consecutive query rows of one request and one
 // head; wave w owns rows 32w .. 32w+31 as two blocks of 16.  Key tiles of
-// 64 positions pass through LDS, double-buffered, by DMA (global_load_lds):
+// 64 positions pass through LDS, double-buffered, by DMA (buffer loads to LDS):
 // K (64 x 128 dims, 16 KB), rope (64 x 64 dims, 8 KB) and V (64 x 128, 16
 // KB).  Row chunks are XOR-swizzled so that the operand reads (16 rows at
 // one 16-byte column) and the transposing V reads are free of bank
@@ -227,7 +228,9 @@ __global__ __launch_bounds__(kMaskThreads) void mha_mask_kernel(BatchArgs b,
 //   O^T  += V^T P^T, P^T straight from the S^T accumulators (bf16), V^T by
 //           transposing LDS reads in the token order the accumulators use.
 // Each wave owns its queries' outputs (128 dims), so no data crosses waves
-// but the K/V tiles.
+// but the K/V tiles.  The loop takes two tiles per pass, one from each stage,
+// so that every LDS read is a lane address plus a constant; a left-out key's
+// score becomes -inf through a bit select on its mask bit, with no branch.
 constexpr int kAttWaves = 4;
 constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kQBlk = 32 * kAttWaves;  // query rows per work-group (32 per wave)
@@ -240,6 +243,7 @@ constexpr float kRescaleMargin = 8.f;        // log2 units
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0); lgkmcnt(0)
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
 
   // the wave's queries: blocks qi = 0, 1 of 16 rows; lane (l16, g) holds
   // query 16 qi + l16, dims 32 kk + 8 g .. +7 (kk < 4: q_nope, else q_rope)
-  int trow[2], vis[2];
+  int trow[2];
   bool live[2];
   v8bf qf[2][6];
 #pragma unroll
@@ -302,7 +306,6 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
     const int r = r0 + 32 * wave + 16 * qi + l16;
     live[qi] = r < n;
     trow[qi] = c0 + min(r, n - 1);
-    vis[qi] = live[qi] ? row_visible(b, bi, trow[qi]) : 0;
     const uint16_t* qn = q_nope + ((int64_t)trow[qi] * kH + h) * kDn + 8 * g;
     const uint16_t* qr = q_rope + ((int64_t)trow[qi] * kH + h) * kDr + 8 * g;
 #pragma unroll
@@ -329,27 +332,32 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
   const uint32_t kv_off = (uint32_t)(kv_row * (kDn * 2) + 16 * ((lane & 15) ^ kv_swz(kv_row)));
   const int r_row = 8 * wave + (lane >> 3);   // row of the wave's first rope load (mod 32)
   const uint32_t r_off = (uint32_t)((lane >> 3) * (kDr * 2) + 16 * ((lane & 7) ^ ((r_row >> 1) & 7)));
-  const unsigned char* kn_b = reinterpret_cast<const unsigned char*>(kn_h);
-  const unsigned char* vn_b = reinterpret_cast<const unsigned char*>(vn_h);
-  const unsigned char* rp_bb = reinterpret_cast<const unsigned char*>(rp_b);
+  // buffer resources over the head's K and V rows and the request's rope
+  // rows: a tile's loads take a lane offset and a scalar row offset
+  const __amdgpu_buffer_rsrc_t kn_r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kn_h), (short)0, lp * (kDn * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vn_r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vn_h), (short)0, lp * (kDn * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rp_r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(rp_b), (short)0, lp * (kDr * 2), 0x00020000);
   auto issue_tile = [&](int tile, int st) {
-    const int64_t key0 = (int64_t)tile * kKTile;
+    const int key0 = tile * kKTile;
 #pragma unroll
     for (int u = 0; u < 40 / kAttWaves; ++u) {
       const int i = wave + kAttWaves * u;  // 0..39: K loads 0..15, rope 16..23, V 24..39
       if (i < 16) {
         // rows 4i .. 4i+3: base row 4i - 4 wave (= 4 kAttWaves u)
-        __builtin_amdgcn_global_load_lds(kn_b + (key0 + 4 * (i - wave)) * (kDn * 2) + kv_off,
-                                         Kn[st] + 1024 * i, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kn_r, (lds_void*)(Kn[st] + 1024 * i), 16, kv_off,
+                                                 (key0 + 4 * (i - wave)) * (kDn * 2), 0, 0);
       } else if (i < 24) {
         const int ii = i - 16;
-        __builtin_amdgcn_global_load_lds(rp_bb + (key0 + 8 * ii) * (kDr * 2) + r_off,
-                                         Rp[st] + 1024 * ii, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_r, (lds_void*)(Rp[st] + 1024 * ii), 16, r_off,
+                                                 (key0 + 8 * ii) * (kDr * 2), 0, 0);
       } else {
         const int ii = i - 24;
         // rows 4 ii .. 4 ii + 3: base row 4 ii - 4 wave
-        __builtin_amdgcn_global_load_lds(vn_b + (key0 + 4 * (ii - wave)) * (kDn * 2) + kv_off,
-                                         Vn[st] + 1024 * ii, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vn_r, (lds_void*)(Vn[st] + 1024 * ii), 16, kv_off,
+                                                 (key0 + 4 * (ii - wave)) * (kDn * 2), 0, 0);
       }
     }
   };
@@ -362,33 +370,31 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
   float m_ref[2] = {-FLT_MAX, -FLT_MAX};
   float l_run[2] = {0.f, 0.f};
 
-  // mask words of a tile, [query block][half]: loaded with the tile's DMA
-  auto mask_words = [&](int tile, uint32_t (&mw)[2][2]) {
+  // The mask holds every word of each row (zeros past the row's visible
+  // positions), so a lane reads its query's two words of a tile with no
+  // test; a lane past the block's end reads the last row's and its results
+  // are dropped.
+  const uint2* mp[2];
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int key_base = tile * kKTile + 32 * half;
-        mw[qi][half] = live[qi] && key_base < vis[qi]
-                           ? mask[(int64_t)trow[qi] * nwords + (key_base >> 5)]
-                           : 0u;
-      }
-  };
-  uint32_t mwn[2][2] = {{0u, 0u}, {0u, 0u}};
+  for (int qi = 0; qi < 2; ++qi)
+    mp[qi] = reinterpret_cast<const uint2*>(mask + (int64_t)trow[qi] * nwords);
+  uint2 mwn[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
   if (ntiles > 0) {
     issue_tile(0, 0);
-    mask_words(0, mwn);
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) mwn[qi] = mp[qi][0];
   }
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int st = tile & 1;
+  // one tile from stage ST (a constant, so that every LDS read takes an
+  // immediate offset on the lane's address)
+  auto tile_step = [&](auto st_c, int tile) {
+    constexpr int st = decltype(st_c)::value;
     __builtin_amdgcn_s_waitcnt(kWaitVmAll);  // this wave's share of the tile has landed
     lds_barrier();                           // every share has; the other stage is free
-    uint32_t mwc[2][2];
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi) mwc[qi][0] = mwn[qi][0], mwc[qi][1] = mwn[qi][1];
+    const uint2 mwc[2] = {mwn[0], mwn[1]};
     if (tile + 1 < ntiles) {
       issue_tile(tile + 1, st ^ 1);
-      mask_words(tile + 1, mwn);
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) mwn[qi] = mp[qi][tile + 1];
     }
     const unsigned char* K = Kn[st];
     const unsigned char* R = Rp[st];
@@ -396,7 +402,6 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int kb0 = 32 * half;  // first key of the half tile within the tile
-      const int key_base = tile * kKTile + kb0;
       // S^T for both query blocks
       v4f s[2][2];
 #pragma unroll
@@ -425,24 +430,19 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
       uint4 pt[2];
 #pragma unroll
       for (int qi = 0; qi < 2; ++qi) {
-        // this lane's keys: key_base + 4 g + r (s[qi][0]) and + 16 (s[qi][1]).
-        // Scores stay unscaled until the exponent (scale_log2 > 0, so the
-        // maximum commutes with it); a block whose 32 keys are all attended
-        // by every query of the wave skips the masking.
-        const uint32_t mw = mwc[qi][half];
+        // this lane's keys: kb0 + 4 g + r (s[qi][0]) and + 16 (s[qi][1]),
+        // bits 4 g + r and 16 + 4 g + r of the half's mask word.  Scores
+        // stay unscaled until the exponent (scale_log2 > 0, so the maximum
+        // commutes with it); a key left out scores -inf, by a bit select on
+        // the mask bit spread over the word.
+        const uint32_t mg = (half ? mwc[qi].y : mwc[qi].x) >> (4 * g);
         float z[8];
-        if (__ballot(mw != ~0u) == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[r] = s[qi][0][r];
-            z[4 + r] = s[qi][1][r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[r] = (mw >> (4 * g + r)) & 1u ? s[qi][0][r] : -INFINITY;
-            z[4 + r] = (mw >> (16 + 4 * g + r)) & 1u ? s[qi][1][r] : -INFINITY;
-          }
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t b0 = (uint32_t)((int)(mg << (31 - r)) >> 31);
+          const uint32_t b1 = (uint32_t)((int)(mg << (15 - r)) >> 31);
+          z[r] = __uint_as_float((__float_as_uint(s[qi][0][r]) & b0) | (0xff800000u & ~b0));
+          z[4 + r] = __uint_as_float((__float_as_uint(s[qi][1][r]) & b1) | (0xff800000u & ~b1));
         }
         float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
                            fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
@@ -490,6 +490,10 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
                                                                 0, 0);
       }
     }
+  };
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    tile_step(std::integral_constant<int, 0>{}, tile);
+    if (tile + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, tile + 1);
   }
 
 #pragma unroll
