@@ -13,9 +13,12 @@
 // tile of 32 selected tokens:
 //   gather   slots come from a per-split table built once (position -> page
 //            -> slot); each 1152-byte row goes straight from HBM into LDS
-//            (global_load_lds, a 1024-byte and a 128-byte piece at a
-//            wave-uniform address; row pitch 1184 bytes) into a ring of three
-//            buffers;
+//            (buffer loads to LDS through a descriptor over the row, a
+//            1024-byte and a 128-byte piece; row pitch 1184 bytes) into a
+//            ring of three buffers.  Buffer loads, not global_load_lds: with
+//            the latter in flight the compiler waits for every outstanding
+//            LDS read (lgkmcnt(0)) wherever it needs one, which defeats the
+//            operand read-ahead below;
 //   S^T      = KV Q^T, wave w taking heads 16w .. 16w+15 (v_mfma_f32_16x16x32_bf16;
 //            the latent part of its query is held in registers, the rope
 //            part in LDS);
@@ -69,6 +72,7 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // V^T operand of a 16-dim block: lane (l16, g) receives dim d0 + l16 of
 // tokens 4g .. 4g+3 and 16+4g .. 16+4g+3, i.e. k = 8g .. 8g+7 in the order
@@ -258,10 +262,11 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
       if (slot < 0) slot = fb;
       const uint16_t* row = kv + (int64_t)slot * DSA_MLA_DIM;
       unsigned char* d = dst + r * kKsPitch;
-      __builtin_amdgcn_global_load_lds(row + 8 * lane, d, 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(row), (short)0, DSA_MLA_DIM * 2, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)d, 16, 16 * lane, 0, 0, 0);
       if (lane < 32)
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const unsigned char*>(row) + tail_ofs, d + 1024, 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(d + 1024), 4, tail_ofs, 0, 0, 0);
     }
   };
 
@@ -366,8 +371,6 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
     }
   };
 
-  // Step `tile`: the value product of `tile` and the scores of `tile + 1`,
-  // while `tile + 2` streams into the third stage.
   // Step `tile`: the value product of `tile` and the scores of `tile + 1`,
   // while `tile + 2` streams into the third stage.  Carried between steps:
   // the token masks of `tile` and `tile + 1`, the slot vector of `tile + 2`.
