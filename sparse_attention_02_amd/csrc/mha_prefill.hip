@@ -51,13 +51,19 @@ __device__ __forceinline__ v8bf as_frag(uint4 u) {
 // of the 128 dims, with its 32 rows of W held in registers for the whole
 // run (the A operands of v_mfma_f32_16x16x32_bf16 for all 16 k-steps), so W
 // is read once.  The latent rows stream through LDS in blocks of 64
-// positions, double-buffered: one 1 KB DMA per row (its 512 latent dims),
-// chunk c of row r stored at chunk c ^ (r & 15) so that the B-operand reads
-// (16 rows at one 16-byte column) are free of bank conflicts.  Each lane
+// positions, double-buffered: one 1 KB DMA per row (its 512 latent dims, a
+// buffer load to LDS through a descriptor over the row), chunk c of row r
+// stored at chunk c ^ (r & 15) so that the B-operand reads (16 rows at one
+// 16-byte column) are free of bank conflicts; a k-step's B operands are
+// read while the previous k-step's products run (buffer loads rather than
+// global_load_lds, with which in flight the compiler would wait for every
+// outstanding LDS read, not only the k-step's).  Each lane
 // ends with 4 consecutive dims of one position: one 8-byte store.  A
 // block's slots and their validity come from its DMA issue (no page-table
 // loads before the stores), and the rope dims of block j are copied by the
 // work-groups of head j mod 128, so no head's work-groups carry all of it.
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kExpPos = 64;
 constexpr int kExpThreads = 512;
 constexpr int kExpRow = kC * 2;  // 1024 bytes of latent per row in LDS
@@ -110,9 +116,11 @@ __global__ __launch_bounds__(kExpThreads, 1) void mha_expand_kernel(
     for (int i = 0; i < kExpPos / 8; ++i) {
       const int r = wave + 8 * i;
       const int slot = __builtin_amdgcn_readlane(my_slot, r);
-      const uint16_t* row = kv + (int64_t)slot * DSA_MLA_DIM;
-      __builtin_amdgcn_global_load_lds(row + 8 * (lane ^ (r & 15)), lat[st] + r * kExpRow, 16, 0,
-                                       0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(kv + (int64_t)slot * DSA_MLA_DIM), (short)0, DSA_MLA_DIM * 2,
+          0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lat[st] + r * kExpRow), 16,
+                                               16 * (lane ^ (r & 15)), 0, 0, 0);
     }
   };
 
@@ -131,19 +139,26 @@ __global__ __launch_bounds__(kExpThreads, 1) void mha_expand_kernel(
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[db][q] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      v8bf bf[4];
+    // the B operands of k-step kk + 1 are read while kk's products run
+    auto read_b = [&](int kk, v8bf (&bf)[4]) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * q + l16;  // r & 15 == l16
         bf[q] = as_frag(*reinterpret_cast<const uint4*>(T + r * kExpRow + 16 * ((4 * kk + g) ^ l16)));
       }
+    };
+    v8bf bf[2][4];
+    read_b(0, bf[0]);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      if (kk + 1 < 16) read_b(kk + 1, bf[(kk + 1) & 1]);
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          acc[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[db][kk], bf[q], acc[db][q], 0, 0, 0);
+          acc[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[db][kk], bf[kk & 1][q], acc[db][q],
+                                                               0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -243,7 +258,6 @@ constexpr float kRescaleMargin = 8.f;        // log2 units
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0); lgkmcnt(0)
