@@ -459,6 +459,39 @@ def summarize_mfma(d, simds=1024):
               f"{100 * b_avg / (a_avg * simds):.1f} |")
 
 
+def summarize_issue(d, cus=256):
+    """Per kernel, from one rocprofv3 --pmc run of SQ_WAVE_CYCLES,
+    SQ_ACTIVE_INST_ANY, SQ_ACTIVE_INST_VALU, SQ_WAIT_INST_ANY, SQ_WAIT_ANY,
+    SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT and GRBM_GUI_ACTIVE: the shares of
+    the waves' lifetime spent issuing (any instruction, VALU) and waiting
+    (for an instruction's operands or a dependency counter, for anything),
+    the LDS unit's active share of the kernel's cycles on each CU, and the
+    bank-conflict share of those LDS cycles."""
+    import collections
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    n_xcd = 8
+    for r in csv.DictReader(open(f)):
+        agg[(_short(r["Kernel_Name"]), _grid(r), r.get("Queue_Id", "?"))][
+            r["Counter_Name"]].append(float(r["Counter_Value"]))
+    print("| kernel | grid (work-items) | queue | dispatches | issuing % | VALU issuing % "
+          "| waiting on operands % | waiting on anything % | LDS active % | LDS bank conflicts % |"
+          "\n|---|---|---|---|---|---|---|---|---|---|")
+    for (k, g, qu), v in agg.items():
+        m = {c: sum(x) / len(x) for c, x in v.items() if x}
+        wc, act = m.get("SQ_WAVE_CYCLES", 0.0), m.get("GRBM_GUI_ACTIVE", 0.0) / n_xcd
+        if wc == 0 or act == 0:
+            continue
+        lds = m.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        pct = lambda c: 100 * m.get(c, 0.0) / wc
+        print(f"| {k} | {g} | {qu} | {len(v['SQ_WAVE_CYCLES'])} | {pct('SQ_ACTIVE_INST_ANY'):.1f} | "
+              f"{pct('SQ_ACTIVE_INST_VALU'):.1f} | {pct('SQ_WAIT_INST_ANY'):.1f} | "
+              f"{pct('SQ_WAIT_ANY'):.1f} | {100 * lds / (act * cus):.1f} | "
+              f"{100 * m.get('SQ_LDS_BANK_CONFLICT', 0.0) / lds if lds else 0.0:.1f} |")
+
+
 # bytes one appended token moves: its bf16 key (256) and latent row (1152)
 # read; its FP8 key (128), scale (4) and latent row (1152) written
 APPEND_BYTES_PER_TOKEN = 2 * 128 + 2 * 576 + 128 + 4 + 2 * 576
@@ -753,6 +786,7 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--summarize-issue", metavar="DIR")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
@@ -760,6 +794,8 @@ def main():
         return summarize_counters(*args.summarize_counters)
     if args.summarize_mfma:
         return summarize_mfma(args.summarize_mfma)
+    if args.summarize_issue:
+        return summarize_issue(args.summarize_issue)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DSA decode path here runs on a single "
               "MI355X (no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
