@@ -559,9 +559,33 @@ __global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(
         if (j < n_split) add(lj[j], u[j], hx[j]);
     }
   } else {
-    for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, lse_of(j));
-    if (mx != -INFINITY)
-      for (int j = 0; j < n_split; ++j) add(lse_of(j), scale_of(j), part_of(j));
+    // batches of 8 splits, each batch's loads issued before any is used
+    // (one round trip per batch, not per split)
+    constexpr int kB = 8;
+    for (int j0 = 0; j0 < n_split; j0 += kB) {
+      float lj[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) lj[u] = lse_of(min(j0 + u, n_split - 1));
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (j0 + u < n_split) mx = fmaxf(mx, lj[u]);
+    }
+    if (mx != -INFINITY) {
+      for (int j0 = 0; j0 < n_split; j0 += kB) {
+        float lj[kB], u_[kB];
+        uint4 hx[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int jj = min(j0 + u, n_split - 1);
+          lj[u] = lse_of(jj);
+          u_[u] = scale_of(jj);
+          hx[u] = part_of(jj);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+          if (j0 + u < n_split) add(lj[u], u_[u], hx[u]);
+      }
+    }
   }
   if (mx == -INFINITY) {
     *reinterpret_cast<uint4*>(o) = make_uint4(0u, 0u, 0u, 0u);
