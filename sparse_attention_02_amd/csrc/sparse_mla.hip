@@ -501,6 +501,9 @@ void sparse_mla_kernel(BatchArgs b, const uint16_t* __restrict__ q, const uint16
 // 8l .. 8l+7 (16-byte loads of the fp16 partials, one 16-byte bf16 store).
 constexpr int kMergeWaves = 8;
 
+// MANY: more than four splits, read in batches of eight (a separate
+// instance, so that the common form keeps its smaller register footprint)
+template <bool MANY>
 __global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(
     const uint16_t* __restrict__ opart, const float* __restrict__ spart,
     const float* __restrict__ lpart, int n_split, int64_t n_th, uint16_t* __restrict__ out,
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(
       a[2 * q + 1] += wj * (f16_hi(wd[q]) * u);
     }
   };
-  if (n_split <= 4) {
+  if (!MANY) {
     // every load issued before any is used
     float lj[4], u[4];
     uint4 hx[4];
@@ -672,8 +675,14 @@ hipError_t launch_sparse_mla(const BatchArgs& b, const uint16_t* q, const uint16
   const int64_t n_th = (int64_t)b.T * DSA_MLA_HEADS;
   const int64_t n_mwg = (n_th + kMergeWaves - 1) / kMergeWaves;
   const int m_per_xcd = (int)((n_mwg + 7) / 8);
-  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(8 * m_per_xcd)),
-                     dim3(64 * kMergeWaves), 0, s, opart, spart, lpart, used, n_th, out, lse, m_per_xcd);
+  if (used <= 4)
+    hipLaunchKernelGGL(mla_merge_kernel<false>, dim3((unsigned)(8 * m_per_xcd)),
+                       dim3(64 * kMergeWaves), 0, s, opart, spart, lpart, used, n_th, out, lse,
+                       m_per_xcd);
+  else
+    hipLaunchKernelGGL(mla_merge_kernel<true>, dim3((unsigned)(8 * m_per_xcd)),
+                       dim3(64 * kMergeWaves), 0, s, opart, spart, lpart, used, n_th, out, lse,
+                       m_per_xcd);
   return hipGetLastError();
 }
 
