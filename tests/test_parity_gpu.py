@@ -284,10 +284,12 @@ def test_selection_end_to_end_small(ci):
 
 
 @pytest.mark.parametrize("ci", [0, 2, 3, 4, 5])
-@pytest.mark.parametrize("n_split", [1, 2, 7])
+@pytest.mark.parametrize("n_split", [1, 2, 7, 13, 64])
 @pytest.mark.parametrize("stress", [False, True])
 def test_sparse_mla_small_oracle_selection(ci, n_split, stress):
-    """Attention fed the oracle's selection, for several split counts;
+    """Attention fed the oracle's selection, for several split counts (the
+    merge reads more than four splits in batches of eight: 7 is one partial
+    batch, 13 a full and a partial one, 64 eight full ones);
     `stress` draws q and kv from N(0,1) so the absolute bound bites."""
     b = _small(SMALL[ci], 500 + ci, mla_scale=1.0 if stress else None)
     d = to_device(b)
