@@ -234,8 +234,8 @@ __global__ __launch_bounds__(kMaskThreads) void mha_mask_kernel(BatchArgs b,
 // K (64 x 128 dims, 16 KB), rope (64 x 64 dims, 8 KB) and V (64 x 128, 16
 // KB).  Row chunks are XOR-swizzled so that the operand reads (16 rows at
 // one 16-byte column) and the transposing V reads are free of bank
-// conflicts: chunk c of K or V row r sits at chunk c ^ kv_swz(r) of the row,
-// chunk c of rope row r at c ^ ((r >> 1) & 7).  Per 32-key half tile:
+// conflicts: chunk c of K row r sits at chunk c ^ (r & 15) of the row, of V
+// row r at c ^ kv_swz(r), of rope row r at c ^ ((r >> 1) & 7).  Per 32-key half tile:
 //   S^T   = K Q^T (keys x queries, 6 k-steps of 32 dims: 4 of K, 2 of rope),
 //           the wave's queries held in registers as B operands;
 //   softmax online per query in fp32, with the mask bits; the reference max
@@ -264,11 +264,15 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 constexpr unsigned kWaitVmAll = 0x0f70;
 constexpr unsigned kWaitLgkmAll = 0xc07f;
 
-// Chunk c (16 bytes) of K or V row r sits at chunk c ^ kv_swz(r) of the row.
-// The 16 rows of an operand read (rows r .. r+15 at one chunk) land on 16
-// distinct chunks, and so do the two-chunk pieces of 8 consecutive rows that
-// one half of a transposing V read covers: both free of bank conflicts.
+// Chunk c (16 bytes) of V row r sits at chunk c ^ kv_swz(r) of the row, of K
+// row r at c ^ k_swz(r).  The two-chunk pieces of 8 consecutive rows that
+// one half of a transposing V read covers land on distinct chunks under
+// kv_swz.  The K operand reads (16 rows at one 16-byte column per 16 lanes,
+// the four 16-lane groups at four columns) are conflict-free under r & 15
+// and take twice the LDS cycles under kv_swz (measured with a probe of the
+// two patterns: 8 against 4 cycles per 16-byte read).
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -332,17 +336,18 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
   // DMA of tile `tile` into stage `st`: 16 + 8 + 16 wave-wide 1 KB loads,
   // 10 per wave.  Load i of K (or V) fills LDS bytes 1024 i .. +1023 = rows
   // 4i .. 4i+3; lane L writes LDS chunk L % 16 of row 4i + L / 16 and so
-  // reads global chunk (L % 16) ^ kv_swz(row).  Rope load i covers rows 8i ..
-  // 8i+7, lane L chunk L % 8 of row 8i + L / 8, from chunk (L % 8) ^ ((row >>
-  // 1) & 7).
+  // reads global chunk (L % 16) ^ k_swz(row) (K) or (L % 16) ^ kv_swz(row)
+  // (V).  Rope load i covers rows 8i .. 8i+7, lane L chunk L % 8 of row 8i +
+  // L / 8, from chunk (L % 8) ^ ((row >> 1) & 7).
   const uint16_t* kn_h = kn + ((int64_t)bi * kH + h) * lp * kDn;
   const uint16_t* vn_h = vn + ((int64_t)bi * kH + h) * lp * kDn;
   const uint16_t* rp_b = rope + (int64_t)bi * lp * kDr;
   // A wave's loads are K/V loads i = wave + 4u and rope loads i = wave + 4u -
-  // 16: kv_swz(row) (K, V) and (row >> 1) & 7 (rope) do not depend on u, so
-  // each lane's byte offset within a load's rows is the same for all of
-  // them and only the scalar base moves.
+  // 16: k_swz(row) (K), kv_swz(row) (V) and (row >> 1) & 7 (rope) do not
+  // depend on u, so each lane's byte offset within a load's rows is the same
+  // for all of them and only the scalar base moves.
   const int kv_row = 4 * wave + (lane >> 4);  // row of the wave's first K/V load
+  const uint32_t kn_off = (uint32_t)(kv_row * (kDn * 2) + 16 * ((lane & 15) ^ k_swz(kv_row)));
   const uint32_t kv_off = (uint32_t)(kv_row * (kDn * 2) + 16 * ((lane & 15) ^ kv_swz(kv_row)));
   const int r_row = 8 * wave + (lane >> 3);   // row of the wave's first rope load (mod 32)
   const uint32_t r_off = (uint32_t)((lane >> 3) * (kDr * 2) + 16 * ((lane & 7) ^ ((r_row >> 1) & 7)));
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
       const int i = wave + kAttWaves * u;  // 0..39: K loads 0..15, rope 16..23, V 24..39
       if (i < 16) {
         // rows 4i .. 4i+3: base row 4i - 4 wave (= 4 kAttWaves u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kn_r, (lds_void*)(Kn[st] + 1024 * i), 16, kv_off,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kn_r, (lds_void*)(Kn[st] + 1024 * i), 16, kn_off,
                                                  (key0 + 4 * (i - wave)) * (kDn * 2), 0, 0);
       } else if (i < 24) {
         const int ii = i - 16;
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void mha_attend_kernel(
         for (int e = 0; e < 2; ++e) {
           const int row = kb0 + 16 * e + l16;
           if (kk < 4) {
-            const int ch = (4 * kk + g) ^ kv_swz(row);
+            const int ch = (4 * kk + g) ^ k_swz(row);
             a[e] = as_frag(*reinterpret_cast<const uint4*>(K + row * (kDn * 2) + 16 * ch));
           } else {
             const int ch = (4 * (kk - 4) + g) ^ ((row >> 1) & 7);
